@@ -1,0 +1,121 @@
+"""Second, independent implementation of the layer in pure Python (lists, math.fsum, math.exp).
+
+TEST INFRASTRUCTURE ONLY.  Written without numpy so that a mistake shared by
+numpy idioms in ``reference`` (an axis, a transpose, a broadcast) cannot hide
+in both.  Only for tiny inputs (N <= 64 tokens).
+"""
+
+from __future__ import annotations
+
+import math
+
+
+def bf16(x: float) -> float:
+    """Nearest bfloat16 (8 significant bits), ties to even, via Python's round-half-even."""
+    if x == 0.0 or math.isinf(x) or math.isnan(x):
+        return x
+    m, e = math.frexp(x)  # x = m * 2**e, 0.5 <= |m| < 1
+    quantum_exp = max(e - 8, -133)
+    r = round(x / 2.0 ** quantum_exp) * 2.0 ** quantum_exp
+    if abs(r) > (2.0 - 2.0 ** -7) * 2.0 ** 127:
+        return math.copysign(math.inf, r)
+    return r
+
+
+def scores(x_cur, x_ref, relative=True, ref_row_offset=0):
+    n = len(x_cur)
+    ref = x_cur if x_ref is None else x_ref
+    out = []
+    for i in range(n):
+        j = i - ref_row_offset
+        if j < 0 or j >= len(ref):
+            out.append(math.inf)
+            continue
+        num = math.fsum(abs(a - b) for a, b in zip(x_cur[i], ref[j]))
+        if not relative:
+            out.append(num)
+            continue
+        den = math.fsum(abs(b) for b in ref[j])
+        if den == 0.0:
+            out.append(0.0 if num == 0.0 else math.inf)
+        else:
+            out.append(num / den)
+    return out
+
+
+def topk(s, k):
+    ranked = sorted(range(len(s)), key=lambda i: (-s[i], i))
+    chosen = set(ranked[:k])
+    return [i in chosen for i in range(len(s))]
+
+
+def compact(mask):
+    return [i for i, m in enumerate(mask) if m], [i for i, m in enumerate(mask) if not m]
+
+
+def matmul_t(x, w_rows):
+    """x @ w.T for lists of rows."""
+    return [[math.fsum(a * b for a, b in zip(row, wr)) for wr in w_rows] for row in x]
+
+
+def project(x_rows, w_qkv, part):
+    d = len(w_qkv[0])
+    off = "qkv".index(part) * d
+    xb = [[bf16(v) for v in row] for row in x_rows]
+    return [[bf16(v) for v in row] for row in matmul_t(xb, w_qkv[off:off + d])]
+
+
+def attention(q, k, v, heads, scale=None):
+    dim = len(q[0])
+    d = dim // heads
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = [[0.0] * dim for _ in q]
+    for h in range(heads):
+        c0 = h * d
+        for i, qi in enumerate(q):
+            s = [scale * math.fsum(qi[c0 + t] * kj[c0 + t] for t in range(d)) for kj in k]
+            mx = max(s)
+            p = [math.exp(x - mx) for x in s]
+            z = math.fsum(p)
+            for t in range(d):
+                out[i][c0 + t] = math.fsum(p[j] * k_v[c0 + t] for j, k_v in enumerate(v)) / z
+    return out
+
+
+def layer_step(x_cur, x_ref, w_qkv, heads, k_cache, v_cache, out, k):
+    """Score, top-k, compact, project, cache sync, attention, scatter -- all in lists."""
+    s = scores(x_cur, x_ref)
+    mask = topk(s, k)
+    idx, pidx = compact(mask)
+    xa = [x_cur[i] for i in idx]
+    q = project(xa, w_qkv, "q")
+    ka = project(xa, w_qkv, "k")
+    va = project(xa, w_qkv, "v")
+    for r, i in enumerate(idx):
+        k_cache[i] = list(ka[r])
+        v_cache[i] = list(va[r])
+    o = attention(q, k_cache, v_cache, heads)
+    for r, i in enumerate(idx):
+        out[i] = list(o[r])
+    return {"scores": s, "mask": mask, "idx": idx, "pidx": pidx, "q": q, "k": ka, "v": va, "o_a": o}
+
+
+def recover(x0_prev, eps, rows, src_row_offset, sigma):
+    res = []
+    for p in rows:
+        j = p - src_row_offset
+        clean = x0_prev[j] if 0 <= j < len(x0_prev) else [0.0] * len(eps[p])
+        res.append([bf16((1.0 - sigma) * a + sigma * b) for a, b in zip(clean, eps[p])])
+    return res
+
+
+def periods_by_rank(s, counts, periods):
+    ranked = sorted(range(len(s)), key=lambda i: (-s[i], i))
+    out = [0] * len(s)
+    pos = 0
+    for c, p in zip(counts, periods):
+        for i in ranked[pos:pos + c]:
+            out[i] = p
+        pos += c
+    return out

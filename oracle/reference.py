@@ -1,0 +1,293 @@
+"""Plain numpy float64 oracle of the token-pruned attention layer.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): slow, obviously
+correct, one function per step, in the order the method runs them.
+
+Conventions
+-----------
+* Token rows are row-major ``[N, D]``; inside Q/K/V, column ``h*d + j`` is
+  dimension ``j`` of head ``h``.
+* ``w_qkv`` is ``[3*D, D]``: rows ``[0, D)`` project to Q, ``[D, 2D)`` to K,
+  ``[2D, 3D)`` to V, and ``y = x @ w_part.T``.
+* Inputs arrive as float64 arrays holding bf16 (or fp32) values exactly.
+  Values the method stores (Q, K, V, recovered rows) are rounded to bf16 at
+  the point where they are stored; scores, softmax and outputs stay float64.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+# Largest finite bfloat16: (2 - 2**-7) * 2**127.
+_BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
+
+
+def round_bf16(x) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16, ties to even (storage rounding).
+
+    bfloat16 keeps 8 significant bits, so a value in [2**(e-1), 2**e) is
+    rounded to a multiple of 2**(e-8); below the smallest normal 2**-126 the
+    spacing stays 2**-133.  Results beyond the largest finite bf16 become
+    +-inf.  Pinned against torch's float32 -> bfloat16 conversion.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = x.copy()
+    fin = np.isfinite(x) & (x != 0.0)
+    v = x[fin]
+    _, e = np.frexp(v)
+    q = np.maximum(e - 8, -133)
+    r = np.ldexp(np.rint(np.ldexp(v, -q)), q)
+    r = np.where(np.abs(r) > _BF16_MAX, np.copysign(np.inf, r), r)
+    out[fin] = r
+    return out
+
+
+# ---------------------------------------------------------------- a1: score
+
+def token_scores(x_cur, x_ref=None, ref_row_offset: int = 0, relative: bool = True) -> np.ndarray:
+    """Per-token change score.
+
+    HSA page §2.1 ("Selección Dinámica"): tokens are ranked by the relative L1
+    change of each token; LIPAR page §2.B: a latent patch is compared by L1
+    norm with the patch at the same spatial location in the previous frame.
+
+    The reference row of token n is ``ref[n - ref_row_offset]`` where ``ref``
+    is ``x_ref`` if given, else ``x_cur`` itself (the inter-frame case, with
+    the offset equal to one frame's H*W tokens).  Tokens without a reference
+    row score +inf (always kept).  Relative score = sum|x - r| / sum|r|, with
+    0/0 -> 0 and x/0 -> +inf; ``relative=False`` returns sum|x - r|.
+    """
+    x_cur = np.asarray(x_cur, dtype=np.float64)
+    ref = x_cur if x_ref is None else np.asarray(x_ref, dtype=np.float64)
+    n = x_cur.shape[0]
+    scores = np.full(n, np.inf)
+    rows = np.arange(max(ref_row_offset, 0), min(n, ref.shape[0] + ref_row_offset))
+    if rows.size == 0:
+        return scores
+    r = ref[rows - ref_row_offset]
+    num = np.abs(x_cur[rows] - r).sum(axis=1)
+    if not relative:
+        scores[rows] = num
+        return scores
+    den = np.abs(r).sum(axis=1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        s = num / den
+    s = np.where(den == 0.0, np.where(num == 0.0, 0.0, np.inf), s)
+    scores[rows] = s
+    return scores
+
+
+# --------------------------------------------------------------- a2: select
+
+def select_topk(scores, k: int) -> np.ndarray:
+    """Mask of the k highest scores; equal scores are taken in ascending token order."""
+    scores = np.asarray(scores, dtype=np.float64)
+    n = scores.shape[0]
+    if not 0 <= k <= n:
+        raise ValueError("k out of range")
+    order = np.lexsort((np.arange(n), -scores))
+    mask = np.zeros(n, dtype=bool)
+    mask[order[:k]] = True
+    return mask
+
+
+def select_threshold(scores, tau: float) -> np.ndarray:
+    """LIPAR page §2.B: a token whose change is below tau is redundant (pruned); s >= tau stays active."""
+    return np.asarray(scores, dtype=np.float64) >= tau
+
+
+def assign_periods(scores, group_counts, group_periods) -> np.ndarray:
+    """HSA page §2.1: split tokens into disjoint groups by score rank, highest change first.
+
+    Group g receives the next ``group_counts[g]`` tokens in (score descending,
+    index ascending) order and the activity period ``group_periods[g]``
+    (= T / s_g, the total step count over the group's step budget).
+    """
+    scores = np.asarray(scores, dtype=np.float64)
+    n = scores.shape[0]
+    if sum(group_counts) != n:
+        raise ValueError("group counts must cover all tokens")
+    order = np.lexsort((np.arange(n), -scores))
+    periods = np.empty(n, dtype=np.int64)
+    start = 0
+    for count, period in zip(group_counts, group_periods):
+        periods[order[start:start + count]] = period
+        start += count
+    return periods
+
+
+def schedule_mask(periods, step: int) -> np.ndarray:
+    """HSA page §2.1: a token of period p = T/s_k is active at global step i iff i mod p == 0."""
+    return (step % np.asarray(periods, dtype=np.int64)) == 0
+
+
+# -------------------------------------------------------------- a3: compact
+
+def compact(mask) -> tuple[np.ndarray, np.ndarray]:
+    """Ascending indices of the active tokens and of the pruned complement (HSA page §2.2, item 1)."""
+    mask = np.asarray(mask, dtype=bool)
+    return np.flatnonzero(mask).astype(np.int64), np.flatnonzero(~mask).astype(np.int64)
+
+
+# ------------------------------------------------------- a4: recovery rows
+
+def recover_rows(x0_prev, eps, rows, src_row_offset: int, sigma: float) -> np.ndarray:
+    """LIPAR page §2.C, noise-aware duplication: a pruned token's context is rebuilt from the
+    clean previous latent at the same location plus fresh noise, R = (1 - sigma) * x0_prev + sigma * eps.
+
+    For token p the clean previous latent is ``x0_prev[p - src_row_offset]``
+    and the noise is ``eps[p]``; a token with no previous row takes 0 for the
+    clean term.  The result is stored, so it is rounded to bf16.
+    """
+    x0_prev = np.asarray(x0_prev, dtype=np.float64)
+    eps = np.asarray(eps, dtype=np.float64)
+    rows = np.asarray(rows, dtype=np.int64)
+    src = rows - src_row_offset
+    ok = (src >= 0) & (src < x0_prev.shape[0])
+    clean = np.zeros((rows.size, eps.shape[1]))
+    clean[ok] = x0_prev[src[ok]]
+    return round_bf16((1.0 - sigma) * clean + sigma * eps[rows])
+
+
+# ----------------------------------------------------------- a5: projection
+
+def project(x_rows, w_qkv, parts: str = "qkv") -> dict:
+    """HSA page §2.2, item 1: only the active tokens go through the Q/K/V projections.
+
+    Returns bf16-rounded ``x_rows @ W_part.T`` for each requested part
+    ('q', 'k', 'v').  The input rows are rounded to bf16 first (fp32 tokens
+    enter the projection as bf16).
+    """
+    x = round_bf16(np.asarray(x_rows, dtype=np.float64))
+    w = np.asarray(w_qkv, dtype=np.float64)
+    d = w.shape[1]
+    if w.shape[0] != 3 * d or x.shape[1] != d:
+        raise ValueError("w_qkv must be [3*D, D] and rows [n, D]")
+    out = {}
+    for i, name in enumerate("qkv"):
+        if name in parts:
+            out[name] = round_bf16(x @ w[i * d:(i + 1) * d].T)
+    return out
+
+
+# --------------------------------------------------------- a6: cache sync
+
+def kv_cache_sync(k_cache, v_cache, rows, k_rows, v_rows) -> None:
+    """HSA page §2.2, item 2: fresh K/V of the given tokens overwrite their rows of the
+    per-layer cache in place; every other row keeps its (stale but valid) entry."""
+    rows = np.asarray(rows, dtype=np.int64)
+    k_cache[rows] = k_rows
+    v_cache[rows] = v_rows
+
+
+# ----------------------------------------------------------- a7: attention
+
+def attention(q, k, v, heads: int, scale: float | None = None, block: int = 256,
+              return_lse: bool = False):
+    """HSA page §2.2, items 3-4: active queries attend over the full cached K/V.
+
+    Per head h: O_h = softmax(Q_h K_h^T * scale) V_h with scale = 1/sqrt(d),
+    no mask (bidirectional).  Float64 throughout; query rows are processed in
+    blocks only to bound memory.  ``lse`` is the natural-log normaliser
+    log(sum_j exp(S_ij)) per (head, query).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    n_q, dim = q.shape
+    d = dim // heads
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    out = np.zeros((n_q, dim))
+    lse = np.zeros((heads, n_q))
+    for h in range(heads):
+        cols = slice(h * d, (h + 1) * d)
+        kh = k[:, cols]
+        vh = v[:, cols]
+        for r0 in range(0, n_q, block):
+            s = (q[r0:r0 + block, cols] @ kh.T) * scale
+            m = s.max(axis=1, keepdims=True)
+            p = np.exp(s - m)
+            z = p.sum(axis=1, keepdims=True)
+            out[r0:r0 + block, cols] = (p @ vh) / z
+            lse[h, r0:r0 + block] = (m + np.log(z))[:, 0]
+    if return_lse:
+        return out, lse
+    return out
+
+
+# ------------------------------------------------------------ a8: scatter
+
+def scatter(out, rows, o_rows) -> None:
+    """Outputs of the active tokens go back to their token rows; other rows keep their
+    previous value (HSA page §2.3: skipped tokens reuse what was cached)."""
+    out[np.asarray(rows, dtype=np.int64)] = o_rows
+
+
+# --------------------------------------------------------- whole-layer steps
+
+def init_kv_cache(x, w_qkv) -> tuple[np.ndarray, np.ndarray]:
+    """Cache at the start of a run: K/V projections of every token of the previous latent."""
+    p = project(x, w_qkv, "kv")
+    return p["k"], p["v"]
+
+
+def layer_step(x_cur, w_qkv, heads: int, k_cache, v_cache, out, *, mask=None, x_ref=None,
+               ref_row_offset: int = 0, k: int | None = None, tau: float | None = None,
+               relative: bool = True) -> dict:
+    """One pruned layer step (HSA page §2.2): score, select, compact, project the active
+    tokens, sync their K/V into the cache, attend, scatter.  Updates the cache and ``out``
+    in place and returns the intermediate results.
+
+    Selection: ``mask`` if given, else top-``k`` if ``k`` is given, else ``s >= tau``.
+    """
+    scores = None
+    if mask is None:
+        scores = token_scores(x_cur, x_ref, ref_row_offset, relative)
+        mask = select_topk(scores, k) if k is not None else select_threshold(scores, tau)
+    idx, pidx = compact(mask)
+    res = {"scores": scores, "mask": np.asarray(mask, bool), "idx": idx, "pidx": pidx}
+    if idx.size == 0:
+        res["o_a"] = np.zeros((0, out.shape[1]))
+        return res
+    p = project(np.asarray(x_cur, dtype=np.float64)[idx], w_qkv, "qkv")
+    kv_cache_sync(k_cache, v_cache, idx, p["k"], p["v"])
+    o_a = attention(p["q"], k_cache, v_cache, heads)
+    scatter(out, idx, o_a)
+    res.update(q=p["q"], k=p["k"], v=p["v"], o_a=o_a)
+    return res
+
+
+def lipar_step(x, eps, w_qkv, heads: int, hw: int, k: int, sigma: float,
+               k_cache, v_cache, out, query_rows=None) -> dict:
+    """One inter-frame pruned pass over a whole clip (LIPAR page §2.B and §2.C).
+
+    Tokens are scored against the same location one frame earlier (offset
+    ``hw``; first-frame tokens score +inf), the top-``k`` stay active; active
+    tokens are projected from their own latent, pruned tokens get K/V from the
+    recovered row (1 - sigma) * x0_prev + sigma * eps.  Every cache row is
+    rewritten; active queries attend over the whole cache.
+
+    ``query_rows`` (positions into the active list) restricts the attention to a
+    sample of active queries; rows are independent given the cache.
+    """
+    scores = token_scores(x, None, hw)
+    mask = select_topk(scores, k)
+    idx, pidx = compact(mask)
+    res = {"scores": scores, "mask": mask, "idx": idx, "pidx": pidx}
+    xa = np.asarray(x, dtype=np.float64)[idx]
+    pa = project(xa, w_qkv, "kv")
+    kv_cache_sync(k_cache, v_cache, idx, pa["k"], pa["v"])
+    if pidx.size:
+        r = recover_rows(x, eps, pidx, hw, sigma)
+        pp = project(r, w_qkv, "kv")
+        kv_cache_sync(k_cache, v_cache, pidx, pp["k"], pp["v"])
+        res.update(r=r, k_p=pp["k"], v_p=pp["v"])
+    if query_rows is not None:
+        xa = xa[np.asarray(query_rows)]
+    q = project(xa, w_qkv, "q")["q"]
+    o_a = attention(q, k_cache, v_cache, heads)
+    if query_rows is None:
+        scatter(out, idx, o_a)
+    res.update(q=q, k=pa["k"], v=pa["v"], o_a=o_a)
+    return res

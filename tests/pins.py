@@ -1,0 +1,211 @@
+"""Checks that pin the oracle to facts other than itself.
+
+Each ``check_*`` takes the implementation under test as arguments, so the same
+check runs on the real oracle (tests/test_oracle.py) and on copies of it with
+a planted mistake (tests/test_oracle_mutations.py), where it must fail.
+Every check raises AssertionError on a mismatch.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from oracle import brute
+
+
+def rng(seed=0):
+    return np.random.default_rng(seed)
+
+
+def bf16_values(a):
+    """float64 array holding bf16-representable values (RNE via torch, a library routine)."""
+    return torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+# ------------------------------------------------------------------ scores
+
+def check_scores(token_scores):
+    r = rng(1)
+    x = bf16_values(r.standard_normal((48, 96)))
+    # identical tokens -> 0
+    assert np.all(token_scores(x, x) == 0.0)
+    # doubling every element (exact in bf16) -> relative change exactly 1
+    assert np.all(token_scores(2.0 * x, x) == 1.0)
+    # x_cur = -x_ref -> sum|2r| / sum|r| = 2 exactly
+    assert np.all(token_scores(-x, x) == 2.0)
+    # a power-of-two rescale of both inputs leaves the relative score bit-identical
+    y = bf16_values(x + 0.3 * r.standard_normal(x.shape))
+    assert np.array_equal(token_scores(y, x), token_scores(8.0 * y, 8.0 * x))
+    # absolute mode scales with the data
+    assert np.allclose(token_scores(8.0 * y, 8.0 * x, relative=False), 8.0 * token_scores(y, x, relative=False))
+    # zero reference rows: 0/0 -> 0, x/0 -> inf
+    z = np.zeros((2, 96))
+    s = token_scores(np.stack([np.zeros(96), np.ones(96)]), z)
+    assert s[0] == 0.0 and math.isinf(s[1])
+    # one planted change of size c in one element of row 5
+    u = x.copy()
+    u[5, 7] += 0.5
+    expect = abs(u[5, 7] - x[5, 7]) / np.abs(x[5]).sum()
+    s = token_scores(u, x)
+    assert abs(s[5] - expect) <= 1e-15 * expect and np.all(np.delete(s, 5) == 0.0)
+    # inter-frame mode: reference is the row hw earlier, first frame is +inf
+    hw = 12
+    s = token_scores(y, None, hw)
+    assert np.all(np.isinf(s[:hw]))
+    expect = [math.fsum(abs(a - b) for a, b in zip(y[i], y[i - hw])) / math.fsum(abs(b) for b in y[i - hw])
+              for i in range(hw, y.shape[0])]
+    assert np.allclose(s[hw:], expect, rtol=1e-14, atol=0)
+    # brute force
+    bs = brute.scores(y.tolist(), x.tolist())
+    assert np.allclose(token_scores(y, x), bs, rtol=1e-14, atol=0)
+
+
+# ------------------------------------------------------------------ select
+
+def check_topk(select_topk):
+    r = rng(2)
+    s = r.random(64)
+    s[[3, 17, 40]] = 0.5  # planted ties
+    s[[8, 9]] = np.inf
+    for k in (0, 1, 2, 5, 20, 63, 64):
+        m = select_topk(s, k)
+        assert m.dtype == bool and m.sum() == k
+        assert np.array_equal(m, np.array(brute.topk(s.tolist(), k)))
+        if 0 < k < 64:
+            assert s[m].min() >= s[~m].max()
+    # ties are taken in ascending token order
+    eq = np.full(10, 0.25)
+    assert np.array_equal(np.flatnonzero(select_topk(eq, 4)), [0, 1, 2, 3])
+    tie = np.array([0.1, 0.5, 0.5, 0.9, 0.5, 0.2])
+    assert np.array_equal(np.flatnonzero(select_topk(tie, 3)), [1, 2, 3])
+
+
+def check_threshold(select_threshold):
+    s = np.array([0.0, 0.1, 0.2, 0.2, 0.3, np.inf])
+    assert np.array_equal(select_threshold(s, 0.2), [False, False, True, True, True, True])
+    assert not select_threshold(np.zeros(5), 1e-9).any()
+
+
+def check_compact(compact):
+    r = rng(3)
+    for n in (0, 1, 63, 200):
+        m = r.random(n) < 0.3
+        idx, pidx = compact(m)
+        bi, bp = brute.compact(m.tolist())
+        assert list(idx) == bi and list(pidx) == bp
+        assert np.array_equal(np.sort(np.concatenate([idx, pidx])), np.arange(n))
+
+
+def check_periods(assign_periods, schedule_mask, golden_rows):
+    # rank groups: 25% / 25% / 50% with periods 1 / 2 / 4
+    r = rng(4)
+    n = 64
+    s = r.random(n)
+    s[[5, 6]] = 0.7
+    per = assign_periods(s, (16, 16, 32), (1, 2, 4))
+    assert list(per) == brute.periods_by_rank(s.tolist(), (16, 16, 32), (1, 2, 4))
+    # the golden schedule table (budget, period, activity per step)
+    for budget, period, acts in golden_rows:
+        for i, a in enumerate(acts):
+            assert bool(schedule_mask(np.array([period]), i)[0]) == bool(a), (budget, i)
+    # closed-form per-step counts on a 25/25/50 split of N
+    n = 32760
+    periods = np.repeat([1, 2, 4], [n // 4, n // 4, n // 2])
+    counts = [int(schedule_mask(periods, i).sum()) for i in range(8)]
+    assert counts == [n, n // 4, n // 2, n // 4, n, n // 4, n // 2, n // 4]
+    assert sum(counts) == 4 * n
+
+
+# ---------------------------------------------------------------- recovery
+
+def check_recover(recover_rows):
+    r = rng(5)
+    x0 = bf16_values(r.standard_normal((30, 16)))
+    eps = bf16_values(r.standard_normal((40, 16)))
+    rows = np.array([10, 11, 25, 39])
+    off = 10
+    # sigma = 0 -> exact clean copy of the previous-frame row; sigma = 1 -> exactly the fresh noise
+    assert np.array_equal(recover_rows(x0, eps, rows, off, 0.0), x0[rows - off])
+    assert np.array_equal(recover_rows(x0, eps, rows, off, 1.0), eps[rows])
+    got = recover_rows(x0, eps, rows, off, 0.6)
+    want = brute.recover(x0.tolist(), eps.tolist(), rows.tolist(), off, 0.6)
+    assert np.array_equal(got, np.array(want))
+    # a row with no previous frame keeps only the noise term
+    got = recover_rows(x0, eps, np.array([3]), off, 0.5)
+    assert np.array_equal(got, np.array(brute.recover(x0.tolist(), eps.tolist(), [3], off, 0.5)))
+
+
+# -------------------------------------------------------------- projection
+
+def check_project(project):
+    r = rng(6)
+    d = 32
+    x = bf16_values(r.standard_normal((20, d)))
+    perm = r.permutation(d)
+    w = np.zeros((3 * d, d))
+    w[:d] = np.eye(d)
+    w[d:2 * d] = 2.0 * np.eye(d)
+    w[2 * d + np.arange(d), perm] = 1.0  # row j of W_v picks input column perm[j]
+    p = project(x, w, "qkv")
+    assert np.array_equal(p["q"], x)
+    assert np.array_equal(p["k"], 2.0 * x)
+    assert np.array_equal(p["v"], x[:, perm])
+    # a general weight vs pure-Python brute force (same storage rounding)
+    w = bf16_values(r.standard_normal((3 * d, d)) / math.sqrt(d))
+    p = project(x, w, "qkv")
+    for part in "qkv":
+        assert np.array_equal(p[part], np.array(brute.project(x.tolist(), w.tolist(), part))), part
+
+
+# --------------------------------------------------------------- attention
+
+def sdpa64(q, k, v, heads):
+    """torch's scaled_dot_product_attention in float64 on the CPU (a library routine)."""
+    n_q, dim = q.shape
+    d = dim // heads
+    tq = torch.from_numpy(q).reshape(n_q, heads, d).permute(1, 0, 2)
+    tk = torch.from_numpy(k).reshape(k.shape[0], heads, d).permute(1, 0, 2)
+    tv = torch.from_numpy(v).reshape(v.shape[0], heads, d).permute(1, 0, 2)
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv)
+    return o.permute(1, 0, 2).reshape(n_q, dim).numpy()
+
+
+def check_attention(attention):
+    r = rng(7)
+    heads, d = 3, 16
+    dim = heads * d
+    q = bf16_values(r.standard_normal((37, dim)))
+    k = bf16_values(r.standard_normal((53, dim)))
+    v = bf16_values(r.standard_normal((53, dim)))
+    o = attention(q, k, v, heads)
+    assert np.allclose(o, sdpa64(q, k, v, heads), rtol=1e-12, atol=1e-12)
+    # value rows all equal c -> output c (rows of softmax sum to one)
+    c = r.standard_normal(dim)
+    assert np.allclose(attention(q, k, np.tile(c, (53, 1)), heads), np.tile(c, (37, 1)), rtol=0, atol=1e-12)
+    # all key rows equal -> uniform weights -> column mean of V
+    ke = np.tile(k[0], (53, 1))
+    assert np.allclose(attention(q, ke, v, heads), np.tile(v.mean(0), (37, 1)), rtol=0, atol=1e-12)
+    # one-hot value columns expose the softmax matrix of head 0: rows sum to 1
+    v1 = np.zeros((53, dim))
+    v1[np.arange(d), np.arange(d)] = 1.0
+    p = attention(q, k, v1, heads)[:, :d]
+    s = (q[:, :d] @ k[:d, :d].T) / math.sqrt(d)
+    full = (q[:, :d] @ k[:, :d].T) / math.sqrt(d)
+    expect = np.exp(s - full.max(1, keepdims=True)) / np.exp(full - full.max(1, keepdims=True)).sum(1, keepdims=True)
+    assert np.allclose(p, expect, rtol=1e-12, atol=1e-14)
+    _, lse = attention(q, k, v, heads, return_lse=True)
+    for h in range(heads):
+        sh = (q[:, h * d:(h + 1) * d] @ k[:, h * d:(h + 1) * d].T) / math.sqrt(d)
+        mx = sh.max(1)
+        assert np.allclose(lse[h], mx + np.log(np.exp(sh - mx[:, None]).sum(1)), rtol=1e-13, atol=1e-13)
+    # permutation equivariance: no positional term
+    pk = r.permutation(53)
+    pq = r.permutation(37)
+    assert np.allclose(attention(q[pq], k[pk], v[pk], heads), o[pq], rtol=1e-12, atol=1e-12)
+    # brute force on a tiny case
+    qs, ks, vs = q[:5], k[:9], v[:9]
+    assert np.allclose(attention(qs, ks, vs, heads), brute.attention(qs.tolist(), ks.tolist(), vs.tolist(), heads),
+                       rtol=1e-12, atol=1e-13)

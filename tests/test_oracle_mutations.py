@@ -1,0 +1,161 @@
+"""Planted mistakes in copies of the oracle must fail the pins (the pins are not vacuous)."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import pins
+from oracle import reference as ref
+from test_oracle import load_golden_schedule
+
+
+def _fails(check, *args):
+    with pytest.raises(AssertionError):
+        check(*args)
+
+
+# ------------------------------------------------------------------ scores
+
+def _scores_wrong_denominator(x_cur, x_ref=None, ref_row_offset=0, relative=True):
+    s = ref.token_scores(x_cur, x_ref, ref_row_offset, relative=False)
+    if not relative:
+        return s
+    x_cur = np.asarray(x_cur, np.float64)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        return s / np.abs(x_cur).sum(1)  # divides by the current row instead of the reference
+
+
+def _scores_no_abs(x_cur, x_ref=None, ref_row_offset=0, relative=True):
+    x_cur = np.asarray(x_cur, np.float64)
+    r = x_cur if x_ref is None else np.asarray(x_ref, np.float64)
+    out = np.full(x_cur.shape[0], np.inf)
+    rows = np.arange(ref_row_offset, x_cur.shape[0])
+    num = (x_cur[rows] - r[rows - ref_row_offset]).sum(1)  # dropped |.|
+    den = np.abs(r[rows - ref_row_offset]).sum(1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        out[rows] = np.where(den == 0, np.where(num == 0, 0.0, np.inf), num / den) if relative else num
+    return out
+
+
+def _scores_wrong_offset(x_cur, x_ref=None, ref_row_offset=0, relative=True):
+    return ref.token_scores(x_cur, x_ref, max(ref_row_offset - 1, 0), relative)
+
+
+@pytest.mark.parametrize("bad", [_scores_wrong_denominator, _scores_no_abs, _scores_wrong_offset])
+def test_score_mutations_caught(bad):
+    _fails(pins.check_scores, bad)
+
+
+# ------------------------------------------------------------------ select
+
+def _topk_ties_descending(scores, k):
+    n = len(scores)
+    order = np.lexsort((-np.arange(n), -np.asarray(scores)))
+    m = np.zeros(n, bool)
+    m[order[:k]] = True
+    return m
+
+
+def _topk_lowest(scores, k):
+    n = len(scores)
+    order = np.lexsort((np.arange(n), np.asarray(scores)))
+    m = np.zeros(n, bool)
+    m[order[:k]] = True
+    return m
+
+
+@pytest.mark.parametrize("bad", [_topk_ties_descending, _topk_lowest])
+def test_topk_mutations_caught(bad):
+    _fails(pins.check_topk, bad)
+
+
+def test_threshold_strict_caught():
+    _fails(pins.check_threshold, lambda s, tau: np.asarray(s) > tau)
+
+
+def test_compact_mutation_caught():
+    def bad(mask):
+        idx, pidx = ref.compact(mask)
+        return idx[::-1], pidx  # descending order
+    _fails(pins.check_compact, bad)
+
+
+def test_schedule_mutations_caught(root):
+    golden = load_golden_schedule(root)
+    _fails(pins.check_periods, ref.assign_periods, lambda p, i: ((i + 1) % np.asarray(p)) == 0, golden)
+
+    def periods_ascending(scores, counts, periods):
+        return ref.assign_periods(-np.asarray(scores), counts, periods)
+    _fails(pins.check_periods, periods_ascending, ref.schedule_mask, golden)
+
+
+# ---------------------------------------------------------------- recovery
+
+def test_recovery_mutations_caught():
+    def swapped(x0, eps, rows, off, sigma):
+        return ref.recover_rows(x0, eps, rows, off, 1.0 - sigma)
+    _fails(pins.check_recover, swapped)
+
+    def no_offset(x0, eps, rows, off, sigma):
+        return ref.recover_rows(x0, eps, rows, 0, sigma)
+    _fails(pins.check_recover, no_offset)
+
+
+# -------------------------------------------------------------- projection
+
+def test_projection_mutations_caught():
+    def untransposed(x_rows, w_qkv, parts="qkv"):
+        x = ref.round_bf16(np.asarray(x_rows, np.float64))
+        d = w_qkv.shape[1]
+        return {n: ref.round_bf16(x @ w_qkv[i * d:(i + 1) * d]) for i, n in enumerate("qkv") if n in parts}
+    _fails(pins.check_project, untransposed)
+
+    def unrounded(x_rows, w_qkv, parts="qkv"):
+        x = np.asarray(x_rows, np.float64)
+        d = w_qkv.shape[1]
+        return {n: x @ w_qkv[i * d:(i + 1) * d].T for i, n in enumerate("qkv") if n in parts}
+    _fails(pins.check_project, unrounded)
+
+    def kv_swapped(x_rows, w_qkv, parts="qkv"):
+        p = ref.project(x_rows, w_qkv, "qkv")
+        p["k"], p["v"] = p["v"], p["k"]
+        return {n: p[n] for n in parts}
+    _fails(pins.check_project, kv_swapped)
+
+
+# --------------------------------------------------------------- attention
+
+def _attn_no_scale(q, k, v, heads, scale=None, block=256, return_lse=False):
+    return ref.attention(q, k, v, heads, scale=1.0, block=block, return_lse=return_lse)
+
+
+def _attn_head0_keys(q, k, v, heads, scale=None, block=256, return_lse=False):
+    d = q.shape[1] // heads
+    k2 = np.tile(np.asarray(k)[:, :d], (1, heads))  # every head uses head 0's keys
+    return ref.attention(q, k2, v, heads, scale, block, return_lse)
+
+
+def _attn_softmax_wrong_axis(q, k, v, heads, scale=None, block=256, return_lse=False):
+    q, k, v = (np.asarray(a, np.float64) for a in (q, k, v))
+    d = q.shape[1] // heads
+    out = np.zeros_like(q)
+    lse = np.zeros((heads, q.shape[0]))
+    for h in range(heads):
+        c = slice(h * d, (h + 1) * d)
+        s = q[:, c] @ k[:, c].T / np.sqrt(d)
+        p = np.exp(s - s.max(0, keepdims=True))
+        p /= p.sum(0, keepdims=True)  # normalised over queries instead of keys
+        out[:, c] = p @ v[:, c]
+        lse[h] = np.log(np.exp(s).sum(1))
+    return (out, lse) if return_lse else out
+
+
+def _attn_no_max_shift_lse(q, k, v, heads, scale=None, block=256, return_lse=False):
+    out, lse = ref.attention(q, k, v, heads, scale, block, True)
+    return (out, lse - 1.0) if return_lse else out
+
+
+@pytest.mark.parametrize("bad", [_attn_no_scale, _attn_head0_keys, _attn_softmax_wrong_axis, _attn_no_max_shift_lse])
+def test_attention_mutations_caught(bad):
+    _fails(pins.check_attention, bad)
