@@ -1,0 +1,227 @@
+/*
+ * tsa.h -- C ABI of the token-pruned self-attention library (libtsa.so, gfx950).
+ *
+ * One pruned attention layer step over video-DiT latent tokens:
+ *   score -> select -> compact -> QKV of the active tokens -> KV-cache sync
+ *   -> attention of the active queries over the whole cache -> scatter.
+ *
+ * Sources, cited by page title and section (gist.science summaries):
+ *   [HSA]   "Resumen Técnico: Asignación de Pasos Heterogénea (HSA) para la
+ *           Generación Eficiente de Video", gist.science/es/paper/2605.06892
+ *   [LIPAR] "Training-free Latent Inter-Frame Pruning with Attention Recovery",
+ *           gist.science/es/paper/2603.05811 (and the Dutch page /nl/)
+ *
+ * Conventions shared by every call
+ *   - Pointers named *device* are device (HBM) addresses owned by the caller;
+ *     the library never allocates, frees or keeps them.  Pointers named *host*
+ *     are read during the call only.
+ *   - Token rows are row-major [rows, dim]; inside Q/K/V, column h*head_dim+j
+ *     is dimension j of head h.  bf16 values are passed as raw 16-bit words
+ *     (tsa_bf16).  Row buffers must be 16-byte aligned.
+ *   - Index lists are int32, ascending, without repeats, within range.  This
+ *     is a precondition (the kernels clamp nothing and do not check it).
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *     enqueues work on it and returns; nothing synchronises.  Device faults
+ *     surface at the caller's next synchronisation.
+ *   - A call with n == 0 rows of work returns TSA_OK and enqueues nothing.
+ *   - Arguments are validated before anything is enqueued; a failed
+ *     validation returns an error code and writes nothing.
+ */
+#ifndef TSA_H
+#define TSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TSA_ABI_VERSION 1
+
+typedef uint16_t tsa_bf16;
+
+typedef enum tsa_status {
+  TSA_OK = 0,
+  TSA_ERR_INVALID_ARG = 1, /* NULL where a buffer is required, unknown enum value */
+  TSA_ERR_SHAPE = 2,       /* sizes out of range or inconsistent */
+  TSA_ERR_DTYPE = 3,       /* element type not supported by this call */
+  TSA_ERR_ALIGNMENT = 4,   /* a row buffer is not 16-byte aligned */
+  TSA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required */
+  TSA_ERR_HIP = 6          /* the HIP runtime refused a launch */
+} tsa_status;
+
+typedef enum tsa_dtype { TSA_F32 = 0, TSA_BF16 = 1 } tsa_dtype;
+
+typedef enum tsa_score_kind {
+  TSA_SCORE_REL_L1 = 0, /* sum|x - r| / sum|r|   ([HSA] §2.1, dynamic token selection) */
+  TSA_SCORE_ABS_L1 = 1  /* sum|x - r|            ([LIPAR] §2.B, L1 change vs threshold) */
+} tsa_score_kind;
+
+typedef enum tsa_select_mode {
+  TSA_SELECT_TOPK = 0,      /* the k highest scores; equal scores taken in ascending token order */
+  TSA_SELECT_THRESHOLD = 1, /* active iff score >= tau; below tau is redundant ([LIPAR] §2.B) */
+  TSA_SELECT_MASK = 2,      /* active iff aux_in[n] != 0 (a caller-given set) */
+  TSA_SELECT_SCHEDULE = 3   /* active iff step mod aux_in[n] == 0, aux_in = period T/s_k ([HSA] §2.1) */
+} tsa_select_mode;
+
+/* Version of this ABI (TSA_ABI_VERSION of the build). */
+int tsa_abi_version(void);
+
+/* Static text for a status code ("unknown status" for other values). */
+const char* tsa_status_string(int status);
+
+/* Bytes of device workspace tsa_select_active / tsa_assign_groups need for n_rows tokens (may be 0). */
+size_t tsa_select_workspace_bytes(int64_t n_rows);
+
+/*
+ * a1-a3: score every token, select the active set A_i, compact it.
+ * [HSA] §2.1 (relative L1 change per token ranks tokens), [LIPAR] §2.B
+ * (L1 change of a latent patch against the same location in the previous
+ * frame; below the threshold the patch is pruned), [HSA] §2.2 item 1 (only
+ * the active subset goes on).
+ *
+ *   x_cur        device, [n_rows, dim] of `dtype` (TSA_F32 or TSA_BF16).
+ *   x_ref        device, [n_rows, dim] of `dtype`, or NULL to use x_cur itself.
+ *   ref_row_offset  the reference row of token n is ref[n - ref_row_offset];
+ *                tokens with no such row (n - offset outside [0, n_rows)) score
+ *                +inf, so top-k and threshold keep them.  0 = same row of x_ref;
+ *                H*W with x_ref = NULL = same location one frame earlier.
+ *   score_kind   tsa_score_kind.  Relative: 0/0 scores 0, x/0 scores +inf.
+ *   mode         tsa_select_mode.  TOPK uses k (0 <= k <= n_rows), THRESHOLD
+ *                uses tau, MASK and SCHEDULE read aux_in (device u8[n_rows])
+ *                and do not compute scores; SCHEDULE also uses `step` (>= 0),
+ *                and a period of 0 means never active.
+ *   scores_out   device f32[n_rows]; required for TOPK and THRESHOLD, unused
+ *                (may be NULL) for MASK and SCHEDULE.
+ *   mask_out     device u8[n_rows] (1 = active), required.
+ *   idx_out      device i32[n_rows] capacity, required: entries [0, n_active)
+ *                are the active tokens in ascending order.
+ *   pidx_out     device i32[n_rows] capacity or NULL: entries
+ *                [0, n_rows - n_active) are the pruned tokens, ascending.
+ *   n_active_out device i32[1], required.
+ *   workspace    device, tsa_select_workspace_bytes(n_rows) bytes (NULL if 0).
+ * Errors: INVALID_ARG, SHAPE (n_rows < 0 or >= 2^31, dim <= 0 or dim % 8,
+ * k out of range, step < 0), DTYPE, ALIGNMENT, WORKSPACE, HIP.
+ */
+tsa_status tsa_select_active(const void* x_cur, const void* x_ref, int64_t ref_row_offset,
+                             int64_t n_rows, int64_t dim, int dtype, int score_kind, int mode,
+                             int64_t k, float tau, const uint8_t* aux_in, int64_t step,
+                             float* scores_out, uint8_t* mask_out, int32_t* idx_out,
+                             int32_t* pidx_out, int32_t* n_active_out, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
+ * [HSA] §2.1: partition the tokens into disjoint groups by score rank
+ * (highest score first, ties in ascending token order): group g takes the
+ * next group_counts[g] tokens and each of its tokens gets the activity period
+ * group_periods[g] (= T / s_g).  The result feeds TSA_SELECT_SCHEDULE.
+ *
+ *   scores         device f32[n] (e.g. scores_out of tsa_select_active).
+ *   n_groups       1..16.
+ *   group_counts   host int64[n_groups], each >= 0, summing to n.
+ *   group_periods  host uint8[n_groups].
+ *   period_out     device u8[n].
+ *   workspace      device, tsa_select_workspace_bytes(n) + n bytes.
+ * Errors: INVALID_ARG, SHAPE, WORKSPACE, HIP.
+ */
+tsa_status tsa_assign_groups(const float* scores, int64_t n, int n_groups,
+                             const int64_t* group_counts, const uint8_t* group_periods,
+                             uint8_t* period_out, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/*
+ * a4-a5 (+ optional a6): project token rows through the fused QKV weight.
+ * [HSA] §2.2 item 1: only the active tokens go through the Q/K/V projections.
+ * [LIPAR] §2.C (noise-aware duplication): a pruned token's K/V come from its
+ * clean previous latent re-noised with fresh noise.
+ *
+ * Row r of the product takes its input from token t = rows[r] (or t = r when
+ * rows is NULL):
+ *   eps == NULL:  A[r] = x[t]                         (x of `x_dtype`, converted to bf16)
+ *   eps != NULL:  A[r] = bf16((1 - sigma) * x[t - src_row_offset] + sigma * eps[t])
+ *                 computed in fp32 and rounded to nearest even; a token whose
+ *                 row t - src_row_offset is outside [0, n_x_rows) takes 0 for
+ *                 the first term.  x must then be TSA_BF16.
+ * and Q/K/V[r] = bf16(A[r] @ W_part^T), fp32 accumulation, nearest-even rounding.
+ *
+ *   x            device [n_x_rows, dim] of x_dtype (TSA_F32 or TSA_BF16).
+ *   rows         device i32[n] token indices into x (each in [0, n_x_rows)), or NULL.
+ *   w_qkv        device bf16 [3*dim, dim]; rows [0,dim) = W_q, [dim,2dim) = W_k,
+ *                [2dim,3dim) = W_v (output feature-major, like a linear layer).
+ *   q_out        device bf16 [n, dim] (compact row r), or NULL to skip Q.
+ *   k_out/v_out  device bf16, required.  out_is_cache == 0: compact [n, dim].
+ *                out_is_cache != 0: the caches [n_cache, dim]; row r is written
+ *                to row rows[r] (rows required, each < n_cache) -- this fuses
+ *                the cache sync (a6) into the projection.
+ *   eps          device bf16 [n_x_rows, dim] or NULL (no recovery).
+ * dim must be a multiple of 64.
+ * Errors: INVALID_ARG, SHAPE, DTYPE, ALIGNMENT, HIP.
+ */
+tsa_status tsa_qkv_active(const void* x, int x_dtype, int64_t n_x_rows, const int32_t* rows,
+                          int64_t n, int64_t dim, const tsa_bf16* w_qkv, tsa_bf16* q_out,
+                          tsa_bf16* k_out, tsa_bf16* v_out, int out_is_cache, int64_t n_cache,
+                          const tsa_bf16* eps, int64_t src_row_offset, float sigma,
+                          void* stream);
+
+/*
+ * a6: [HSA] §2.2 item 2 -- the fresh K/V of the active tokens overwrite
+ * their rows of the per-layer cache; every other row keeps its stale entry.
+ *   k_a, v_a          device bf16 [n, dim] (compact, row r belongs to token rows[r]).
+ *   rows              device i32[n], each in [0, n_cache).
+ *   k_cache, v_cache  device bf16 [n_cache, dim], updated in place.
+ * dim must be a multiple of 8.  Errors: INVALID_ARG, SHAPE, ALIGNMENT, HIP.
+ */
+tsa_status tsa_kv_cache_sync(const tsa_bf16* k_a, const tsa_bf16* v_a, const int32_t* rows,
+                             int64_t n, tsa_bf16* k_cache, tsa_bf16* v_cache, int64_t n_cache,
+                             int64_t dim, void* stream);
+
+/*
+ * a7: [HSA] §2.2 items 3-4 -- the active queries attend over the full cached
+ * K/V (fresh rows for active tokens, stale rows for skipped ones); cost
+ * O(|A_i| * N) instead of O(N^2).  Per head h:
+ *   O[r, h] = softmax_j(scale * Q[r, h] . K[j, h]) V[j, h],  j over all n_kv rows,
+ * no mask (bidirectional).  bf16 inputs, fp32 accumulation and softmax,
+ * bf16 output (nearest even).
+ *
+ *   q        device bf16 [n_q, heads*head_dim].
+ *   k_cache, v_cache  device bf16 [n_kv, heads*head_dim], n_kv >= 1.
+ *   head_dim 64 or 128; heads >= 1.
+ *   scale    > 0, or <= 0 for 1/sqrt(head_dim).
+ *   out      device bf16: out_rows == NULL: compact [n_q, dim];
+ *            otherwise [n_out, dim] with row r written to row out_rows[r]
+ *            (this fuses the scatter, a8); other rows are not touched.
+ *   lse_out  device f32 [heads, n_q] natural-log normaliser log sum_j exp(scale*s_j), or NULL.
+ * Errors: INVALID_ARG, SHAPE, ALIGNMENT, HIP.
+ */
+tsa_status tsa_sparse_query_attention(const tsa_bf16* q, const tsa_bf16* k_cache,
+                                      const tsa_bf16* v_cache, int64_t n_q, int64_t n_kv,
+                                      int heads, int head_dim, float scale, tsa_bf16* out,
+                                      const int32_t* out_rows, int64_t n_out, float* lse_out,
+                                      void* stream);
+
+/*
+ * a8: outputs of the active tokens go back to token order; rows not listed
+ * keep their previous value ([HSA] §2.3: skipped tokens reuse what was cached).
+ *   o_a   device bf16 [n, dim];  rows device i32[n] in [0, n_out);  out device bf16 [n_out, dim].
+ * dim must be a multiple of 8.  Errors: INVALID_ARG, SHAPE, ALIGNMENT, HIP.
+ */
+tsa_status tsa_scatter_out(const tsa_bf16* o_a, const int32_t* rows, int64_t n, tsa_bf16* out,
+                           int64_t n_out, int64_t dim, void* stream);
+
+/*
+ * a4 alone (for measurement and for callers that keep a compact copy):
+ * dst[r] = bf16 row source of token rows[r], with the same row-source rules
+ * as tsa_qkv_active (plain gather, or recovery when eps != NULL).
+ *   x    device bf16 [n_x_rows, dim];  rows device i32[n];  dst device bf16 [n, dim].
+ * dim must be a multiple of 8.  Errors: INVALID_ARG, SHAPE, ALIGNMENT, HIP.
+ */
+tsa_status tsa_gather_rows(const tsa_bf16* x, int64_t n_x_rows, const int32_t* rows, int64_t n,
+                           int64_t dim, const tsa_bf16* eps, int64_t src_row_offset, float sigma,
+                           tsa_bf16* dst, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TSA_H */

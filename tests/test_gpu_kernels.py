@@ -1,0 +1,394 @@
+"""Per-stage GPU parity against the CPU oracle (through the C ABI)."""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import gpu_util as G
+import pins
+from oracle import reference as ref
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    G.need_gpu()
+
+
+def tsa():
+    import token_sparse_attention_rel_amd as t
+    return t
+
+
+def _randn_bf16(gen, *shape, scale=1.0):
+    return (torch.randn(*shape, generator=gen) * scale).to(torch.bfloat16)
+
+
+# ------------------------------------------------------------------ scores
+
+@pytest.mark.parametrize("dtype,n,dim", [(torch.float32, 256, 128), (torch.bfloat16, 1000, 1536),
+                                         (torch.bfloat16, 77, 5120)])
+def test_scores_match_oracle(dtype, n, dim):
+    t = tsa()
+    g = torch.Generator().manual_seed(n + dim)
+    x_ref = torch.randn(n, dim, generator=g).to(dtype)
+    scale = torch.where(torch.rand(n, generator=g) < 0.7, 0.01, 0.5)
+    x_cur = (x_ref.float() + scale[:, None] * torch.randn(n, dim, generator=g)).to(dtype)
+    x_cur[3] = x_ref[3]           # unchanged token -> 0
+    x_ref[5] = 0
+    x_cur[5] = 0                  # 0 / 0 -> 0
+    x_ref[6] = 0                  # x / 0 -> inf
+    xc, xr = G.dev(x_cur), G.dev(x_ref)
+    scores = torch.empty(n, device="cuda")
+    mask = torch.empty(n, dtype=torch.uint8, device="cuda")
+    idx = torch.empty(n, dtype=torch.int32, device="cuda")
+    na = torch.empty(1, dtype=torch.int32, device="cuda")
+    for kind, rel in ((t.SCORE_REL_L1, True), (t.SCORE_ABS_L1, False)):
+        t.select_active(xc, xr, 0, t.SELECT_TOPK, k=n // 4, score_kind=kind, scores_out=scores,
+                        mask_out=mask, idx_out=idx, n_active_out=na)
+        got = G.host64(scores)
+        want = ref.token_scores(G.host64(x_cur), G.host64(x_ref), 0, relative=rel)
+        fin = np.isfinite(want)
+        assert np.array_equal(np.isfinite(got), fin)
+        assert np.all(np.isinf(got[~fin]))
+        err = np.abs(got[fin] - want[fin]) / np.maximum(np.abs(want[fin]), 1e-30)
+        print(f"  kind={kind} max rel err {err.max():.2e}", flush=True)
+        assert err.max() <= G.SCORE_RTOL
+        if rel:
+            assert got[3] == 0.0 and got[5] == 0.0 and math.isinf(got[6])
+
+
+def test_scores_interframe_offset():
+    t = tsa()
+    g = torch.Generator().manual_seed(5)
+    hw, frames, dim = 40, 5, 256
+    x = torch.randn(hw * frames, dim, generator=g).to(torch.bfloat16)
+    n = x.shape[0]
+    scores = torch.empty(n, device="cuda")
+    mask = torch.empty(n, dtype=torch.uint8, device="cuda")
+    idx = torch.empty(n, dtype=torch.int32, device="cuda")
+    na = torch.empty(1, dtype=torch.int32, device="cuda")
+    t.select_active(G.dev(x), None, hw, t.SELECT_TOPK, k=50, scores_out=scores, mask_out=mask,
+                    idx_out=idx, n_active_out=na)
+    got = G.host64(scores)
+    want = ref.token_scores(G.host64(x), None, hw)
+    assert np.all(np.isinf(got[:hw])) and np.all(np.isfinite(got[hw:]))
+    assert np.max(np.abs(got[hw:] - want[hw:]) / want[hw:]) <= G.SCORE_RTOL
+
+
+# ------------------------------------------------------------------ select
+
+def _exact_score_rows(values, dim=64, seed=0):
+    """fp32 token pairs whose relative L1 score is exactly `values[i]` (a power of two or 0):
+    x_cur = x_ref * (1 + v), exact in fp32 for bf16-valued x_ref."""
+    g = torch.Generator().manual_seed(seed)
+    x_ref = torch.randn(len(values), dim, generator=g).to(torch.bfloat16).float()
+    v = torch.tensor(values, dtype=torch.float32)
+    x_cur = x_ref * (1.0 + v[:, None])
+    return x_cur, x_ref
+
+
+@pytest.mark.parametrize("n", [1, 7, 100, 4096, 4099, 20000])
+def test_topk_select_and_compact_bit_exact_with_ties(n):
+    t = tsa()
+    r = np.random.default_rng(n)
+    # scores drawn from a few exact powers of two -> heavy ties at the k-th value
+    vals = (2.0 ** -r.integers(1, 6, n)).astype(np.float64)
+    vals[r.random(n) < 0.05] = 0.0
+    x_cur, x_ref = _exact_score_rows(vals.tolist(), seed=n)
+    want_scores = ref.token_scores(x_cur.double().numpy(), x_ref.double().numpy())
+    assert np.array_equal(want_scores, vals)  # the construction is exact
+    xc, xr = G.dev(x_cur), G.dev(x_ref)
+    scores = torch.empty(n, device="cuda")
+    mask = torch.empty(n, dtype=torch.uint8, device="cuda")
+    idx = torch.full((n,), -7, dtype=torch.int32, device="cuda")
+    pidx = torch.full((n,), -7, dtype=torch.int32, device="cuda")
+    na = torch.empty(1, dtype=torch.int32, device="cuda")
+    for k in sorted({0, 1, n // 3, n // 2, n - 1, n}):
+        if k < 0:
+            continue
+        t.select_active(xc, xr, 0, t.SELECT_TOPK, k=k, scores_out=scores, mask_out=mask,
+                        idx_out=idx, pidx_out=pidx, n_active_out=na)
+        torch.cuda.synchronize()
+        assert np.array_equal(G.host64(scores), vals)
+        want = ref.select_topk(vals, k)
+        wi, wp = ref.compact(want)
+        assert np.array_equal(mask.cpu().numpy().astype(bool), want), k
+        assert int(na.item()) == k
+        assert np.array_equal(idx.cpu().numpy()[:k], wi)
+        assert np.array_equal(pidx.cpu().numpy()[:n - k], wp)
+
+
+@pytest.mark.parametrize("n", [5, 1023, 4096, 30001])
+def test_threshold_mask_schedule_modes_bit_exact(n):
+    t = tsa()
+    r = np.random.default_rng(7 + n)
+    vals = (2.0 ** -r.integers(1, 8, n)).astype(np.float64)
+    x_cur, x_ref = _exact_score_rows(vals.tolist(), seed=n)
+    xc, xr = G.dev(x_cur), G.dev(x_ref)
+    scores = torch.empty(n, device="cuda")
+    mask = torch.empty(n, dtype=torch.uint8, device="cuda")
+    idx = torch.empty(n, dtype=torch.int32, device="cuda")
+    pidx = torch.empty(n, dtype=torch.int32, device="cuda")
+    na = torch.empty(1, dtype=torch.int32, device="cuda")
+
+    def check(want):
+        torch.cuda.synchronize()
+        wi, wp = ref.compact(want)
+        assert np.array_equal(mask.cpu().numpy().astype(bool), want)
+        assert int(na.item()) == wi.size
+        assert np.array_equal(idx.cpu().numpy()[:wi.size], wi)
+        assert np.array_equal(pidx.cpu().numpy()[:wp.size], wp)
+
+    for tau in (2.0 ** -3, 2.0 ** -3 + 1e-4, 1.0, 0.0):  # exact equality s == tau is active
+        t.select_active(xc, xr, 0, t.SELECT_THRESHOLD, tau=tau, scores_out=scores, mask_out=mask,
+                        idx_out=idx, pidx_out=pidx, n_active_out=na)
+        check(ref.select_threshold(vals, tau))
+    m = r.random(n) < 0.3
+    t.select_active(None, None, 0, t.SELECT_MASK, aux_in=G.dev(torch.from_numpy(m.astype(np.uint8))),
+                    mask_out=mask, idx_out=idx, pidx_out=pidx, n_active_out=na, n_rows=n)
+    check(m)
+    periods = r.choice([1, 2, 4, 0], n).astype(np.uint8)
+    pd = G.dev(torch.from_numpy(periods))
+    for step in range(9):
+        t.select_active(None, None, 0, t.SELECT_SCHEDULE, aux_in=pd, step=step, mask_out=mask,
+                        idx_out=idx, pidx_out=pidx, n_active_out=na, n_rows=n)
+        want = (periods != 0) & (step % np.maximum(periods, 1) == 0)
+        check(want)
+
+
+def test_assign_groups_bit_exact():
+    t = tsa()
+    n = 5000
+    r = np.random.default_rng(3)
+    vals = (2.0 ** -r.integers(1, 5, n)).astype(np.float64)
+    x_cur, x_ref = _exact_score_rows(vals.tolist(), seed=3)
+    scores = torch.empty(n, device="cuda")
+    mask = torch.empty(n, dtype=torch.uint8, device="cuda")
+    idx = torch.empty(n, dtype=torch.int32, device="cuda")
+    na = torch.empty(1, dtype=torch.int32, device="cuda")
+    t.select_active(G.dev(x_cur), G.dev(x_ref), 0, t.SELECT_TOPK, k=1, scores_out=scores,
+                    mask_out=mask, idx_out=idx, n_active_out=na)
+    period = torch.empty(n, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(t.select_workspace_bytes(n) + n, dtype=torch.uint8, device="cuda")
+    for counts, periods in (((1250, 1250, 2500), (1, 2, 4)), ((n,), (3,)), ((0, 4999, 1), (1, 2, 8))):
+        t.assign_groups(scores, counts, periods, period, ws)
+        want = ref.assign_periods(vals, counts, periods)
+        assert np.array_equal(period.cpu().numpy(), want)
+
+
+# -------------------------------------------------------------- row movers
+
+def test_gather_cache_sync_scatter_bit_exact():
+    t = tsa()
+    g = torch.Generator().manual_seed(11)
+    n, dim, na_ = 3000, 1536, 901
+    x = _randn_bf16(g, n, dim)
+    rows = torch.from_numpy(np.sort(np.random.default_rng(1).choice(n, na_, replace=False)).astype(np.int32))
+    xd, rd = G.dev(x), G.dev(rows)
+    dst = torch.empty(na_, dim, dtype=torch.bfloat16, device="cuda")
+    t.gather_rows(xd, rd, na_, dst)
+    assert torch.equal(dst.cpu(), x[rows.long()])
+    # recovery rows: (1 - sigma) x[t - off] + sigma eps[t], first rows have no previous row
+    eps = _randn_bf16(g, n, dim)
+    off = 500
+    for sigma in (0.0, 1.0, 0.6):
+        t.gather_rows(xd, rd, na_, dst, eps=G.dev(eps), src_row_offset=off, sigma=sigma)
+        want = ref.recover_rows(G.host64(x), G.host64(eps), rows.numpy(), off, sigma)
+        got = G.host64(dst)
+        if sigma in (0.0, 1.0):
+            assert np.array_equal(got, want)
+        else:
+            # fp32 evaluation of (1 - s) c + s e: one bf16 ulp of the result plus the fp32
+            # rounding of the two products, which dominates where the terms cancel
+            src = rows.numpy() - off
+            clean = np.where((src >= 0)[:, None], G.host64(x)[np.maximum(src, 0)], 0.0)
+            e = G.host64(eps)[rows.numpy()]
+            ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(want), 2.0 ** -126))) - 7)
+            bound = ulp + 2.0 ** -22 * ((1 - sigma) * np.abs(clean) + sigma * np.abs(e))
+            err = np.abs(got - want)
+            print(f"  recovery sigma={sigma}: {(err > 0).sum()} of {got.size} differ, "
+                  f"max err/bound {np.max(err / bound):.3f}", flush=True)
+            assert np.all(err <= bound)
+    # cache sync: listed rows overwritten, all others bit-identical
+    kc, vc = _randn_bf16(g, n, dim), _randn_bf16(g, n, dim)
+    ka, va = _randn_bf16(g, na_, dim), _randn_bf16(g, na_, dim)
+    kcd, vcd = G.dev(kc), G.dev(vc)
+    t.kv_cache_sync(G.dev(ka), G.dev(va), rd, na_, kcd, vcd)
+    wk, wv = kc.clone(), vc.clone()
+    wk[rows.long()] = ka
+    wv[rows.long()] = va
+    assert torch.equal(kcd.cpu(), wk) and torch.equal(vcd.cpu(), wv)
+    # scatter
+    out = _randn_bf16(g, n, dim)
+    od = G.dev(out)
+    t.scatter_out(G.dev(ka), rd, na_, od)
+    wo = out.clone()
+    wo[rows.long()] = ka
+    assert torch.equal(od.cpu(), wo)
+    # n = 0 touches nothing
+    t.kv_cache_sync(G.dev(ka), G.dev(va), rd, 0, kcd, vcd)
+    t.scatter_out(G.dev(ka), rd, 0, od)
+    assert torch.equal(kcd.cpu(), wk) and torch.equal(od.cpu(), wo)
+
+
+# -------------------------------------------------------------- projection
+
+def test_qkv_layout_exact_with_identity_weights():
+    t = tsa()
+    g = torch.Generator().manual_seed(2)
+    n, dim = 300, 128
+    x = _randn_bf16(g, n, dim)
+    perm = torch.randperm(dim, generator=g)
+    w = torch.zeros(3 * dim, dim)
+    w[:dim] = torch.eye(dim)
+    w[dim:2 * dim] = 2 * torch.eye(dim)
+    w[2 * dim + torch.arange(dim), perm] = 1.0
+    rows = torch.arange(0, n, 3, dtype=torch.int32)
+    m = rows.numel()
+    q = torch.empty(m, dim, dtype=torch.bfloat16, device="cuda")
+    k = torch.empty_like(q)
+    v = torch.empty_like(q)
+    t.qkv_active(G.dev(x), G.dev(rows), m, G.dev(w.to(torch.bfloat16)), q_out=q, k_out=k, v_out=v)
+    xs = x[rows.long()]
+    assert torch.equal(q.cpu(), xs)
+    assert torch.equal(k.cpu(), (2 * xs.float()).to(torch.bfloat16))
+    assert torch.equal(v.cpu(), xs[:, perm])
+
+
+@pytest.mark.parametrize("n_x,m,dim,src", [(256, 64, 128, "f32"), (3000, 901, 1536, "bf16"),
+                                           (700, 131, 5120, "bf16"), (2000, 777, 3072, "recover"),
+                                           (500, 500, 192, "bf16")])
+def test_qkv_matches_oracle(n_x, m, dim, src):
+    t = tsa()
+    g = torch.Generator().manual_seed(m)
+    x = torch.randn(n_x, dim, generator=g)
+    x = x if src == "f32" else x.to(torch.bfloat16)
+    w = (torch.randn(3 * dim, dim, generator=g) / math.sqrt(dim)).to(torch.bfloat16)
+    rows = np.sort(np.random.default_rng(m).choice(n_x, m, replace=False)).astype(np.int32)
+    rd = G.dev(torch.from_numpy(rows))
+    q = torch.empty(m, dim, dtype=torch.bfloat16, device="cuda")
+    k = torch.empty_like(q)
+    v = torch.empty_like(q)
+    eps = None
+    off, sigma = n_x // 10, 0.6
+    if src == "recover":
+        eps = _randn_bf16(g, n_x, dim)
+        t.qkv_active(G.dev(x), rd, m, G.dev(w), q_out=q, k_out=k, v_out=v, eps=G.dev(eps),
+                     src_row_offset=off, sigma=sigma)
+        a_rows = ref.recover_rows(G.host64(x), G.host64(eps), rows, off, sigma)
+    else:
+        t.qkv_active(G.dev(x), rd, m, G.dev(w), q_out=q, k_out=k, v_out=v)
+        a_rows = G.host64(x)[rows]
+    want = ref.project(a_rows, G.host64(w))
+    for name, got in (("q", q), ("k", k), ("v", v)):
+        gh = G.host64(got)
+        if src == "recover":
+            # the recovered input rows carry their own fp32 rounding (see the gather test)
+            G.assert_close(gh, want[name], f"{src} {name}")
+        else:
+            G.assert_bf16_close(gh, want[name], f"{src} {name}")
+    # K/V only, written into cache rows (fused cache sync); other rows untouched
+    kc = _randn_bf16(g, n_x, dim)
+    vc = _randn_bf16(g, n_x, dim)
+    kcd, vcd = G.dev(kc), G.dev(vc)
+    if src == "recover":
+        t.qkv_active(G.dev(x), rd, m, G.dev(w), k_out=kcd, v_out=vcd, out_is_cache=True,
+                     n_cache=n_x, eps=G.dev(eps), src_row_offset=off, sigma=sigma)
+    else:
+        t.qkv_active(G.dev(x), rd, m, G.dev(w), k_out=kcd, v_out=vcd, out_is_cache=True, n_cache=n_x)
+    others = np.setdiff1d(np.arange(n_x), rows)
+    kch, vch = kcd.cpu(), vcd.cpu()
+    assert torch.equal(kch[others], kc[others]) and torch.equal(vch[others], vc[others])
+    assert torch.equal(kch[rows], k.cpu()) and torch.equal(vch[rows], v.cpu())
+
+
+# --------------------------------------------------------------- attention
+
+@pytest.mark.parametrize("n_q,n_kv,heads,hd", [(1, 1, 1, 64), (37, 53, 3, 64), (128, 64, 2, 128),
+                                               (300, 1000, 2, 128), (1000, 4099, 4, 128),
+                                               (777, 2085, 4, 64), (129, 20000, 1, 128)])
+def test_attention_matches_oracle(n_q, n_kv, heads, hd):
+    t = tsa()
+    g = torch.Generator().manual_seed(n_q * 7 + n_kv)
+    dim = heads * hd
+    q = _randn_bf16(g, n_q, dim)
+    k = _randn_bf16(g, n_kv, dim)
+    v = _randn_bf16(g, n_kv, dim)
+    out = torch.empty(n_q, dim, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(heads, n_q, dtype=torch.float32, device="cuda")
+    t.sparse_query_attention(G.dev(q), G.dev(k), G.dev(v), n_q, heads, hd, out, lse_out=lse)
+    want, want_lse = ref.attention(G.host64(q), G.host64(k), G.host64(v), heads, return_lse=True)
+    G.assert_close(G.host64(out), want, f"attn {n_q}x{n_kv} h{heads} d{hd}")
+    assert np.max(np.abs(G.host64(lse) - want_lse)) <= 1e-3 * max(1.0, np.abs(want_lse).max())
+
+
+def test_attention_scaled_inputs_and_scale_argument():
+    """Large logits (sharp softmax) and an explicit scale."""
+    t = tsa()
+    g = torch.Generator().manual_seed(9)
+    n_q, n_kv, heads, hd = 200, 700, 2, 128
+    q = _randn_bf16(g, n_q, heads * hd, scale=3.0)
+    k = _randn_bf16(g, n_kv, heads * hd, scale=3.0)
+    v = _randn_bf16(g, n_kv, heads * hd)
+    out = torch.empty(n_q, heads * hd, dtype=torch.bfloat16, device="cuda")
+    for scale in (0.0, 0.05):
+        t.sparse_query_attention(G.dev(q), G.dev(k), G.dev(v), n_q, heads, hd, out, scale=scale)
+        want = ref.attention(G.host64(q), G.host64(k), G.host64(v), heads,
+                             scale=None if scale == 0.0 else scale)
+        G.assert_close(G.host64(out), want, f"scale={scale}")
+
+
+def test_attention_special_cases():
+    t = tsa()
+    g = torch.Generator().manual_seed(10)
+    n_q, n_kv, heads, hd = 100, 333, 2, 64
+    dim = heads * hd
+    q = _randn_bf16(g, n_q, dim)
+    k = _randn_bf16(g, n_kv, dim)
+    # value rows all equal c -> output c
+    c = _randn_bf16(g, 1, dim)
+    out = torch.empty(n_q, dim, dtype=torch.bfloat16, device="cuda")
+    t.sparse_query_attention(G.dev(q), G.dev(k), G.dev(c.repeat(n_kv, 1)), n_q, heads, hd, out)
+    G.assert_close(G.host64(out), np.tile(G.host64(c), (n_q, 1)), "constant V", rel=4e-3, mabs=1e-2)
+    # all key rows equal -> mean of V
+    v = _randn_bf16(g, n_kv, dim)
+    t.sparse_query_attention(G.dev(q), G.dev(k[:1].repeat(n_kv, 1)), G.dev(v), n_q, heads, hd, out)
+    G.assert_close(G.host64(out), np.tile(G.host64(v).mean(0), (n_q, 1)), "equal K")
+
+
+def test_attention_fused_scatter_leaves_other_rows():
+    t = tsa()
+    g = torch.Generator().manual_seed(12)
+    n, heads, hd = 900, 2, 128
+    dim = heads * hd
+    rows = np.sort(np.random.default_rng(2).choice(n, 250, replace=False)).astype(np.int32)
+    q = _randn_bf16(g, rows.size, dim)
+    k = _randn_bf16(g, n, dim)
+    v = _randn_bf16(g, n, dim)
+    base = _randn_bf16(g, n, dim)
+    out = G.dev(base)
+    t.sparse_query_attention(G.dev(q), G.dev(k), G.dev(v), rows.size, heads, hd, out,
+                             out_rows=G.dev(torch.from_numpy(rows)))
+    oh = out.cpu()
+    others = np.setdiff1d(np.arange(n), rows)
+    assert torch.equal(oh[others], base[others])
+    want = ref.attention(G.host64(q), G.host64(k), G.host64(v), heads)
+    G.assert_close(G.host64(oh)[rows], want, "fused scatter")
+
+
+def test_attention_deterministic():
+    t = tsa()
+    g = torch.Generator().manual_seed(13)
+    n_q, n_kv, heads, hd = 500, 3000, 3, 128
+    q, k, v = (G.dev(_randn_bf16(g, s, heads * hd)) for s in (n_q, n_kv, n_kv))
+    o1 = torch.empty(n_q, heads * hd, dtype=torch.bfloat16, device="cuda")
+    o2 = torch.empty_like(o1)
+    t.sparse_query_attention(q, k, v, n_q, heads, hd, o1)
+    t.sparse_query_attention(q, k, v, n_q, heads, hd, o2)
+    assert torch.equal(o1, o2)

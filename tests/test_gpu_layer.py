@@ -1,0 +1,257 @@
+"""End-to-end GPU parity of the pruned layer step against the CPU oracle.
+
+Small workloads are compared element by element; the full-size workloads are
+run exactly as the benchmark runs them and compared on the whole index lists,
+the whole cache and a seeded sample of output rows (rows are independent
+given the cache, so the oracle computes just those).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import gpu_util as G
+from oracle import reference as ref
+from workloads import configs, generate
+from workloads.configs import scaled
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    G.need_gpu()
+
+
+def tsa():
+    import token_sparse_attention_rel_amd as t
+    return t
+
+
+def _step_case(cfg, seed=0, fused=True, sample=None):
+    """Run one top-k step on the GPU and the oracle; compare."""
+    t = tsa()
+    print(f"  case {cfg.name} N={cfg.n} D={cfg.dim} H={cfg.heads} k={cfg.n_active} seed={seed}", flush=True)
+    inp = generate.step_inputs(cfg, seed)
+    x_prev, x_cur, w = inp["x_prev"], inp["x_cur"], inp["w_qkv"]
+    layer = t.PrunedAttentionLayer(cfg.n, cfg.dim, cfg.heads, G.dev(w))
+    xp, xc = G.dev(x_prev), G.dev(x_cur)
+    layer.init_cache(xp)
+    torch.cuda.synchronize()
+    k_init, v_init = G.host64(layer.k_cache), G.host64(layer.v_cache)
+    layer.step_topk(xc, xp, cfg.n_active, fused=fused)
+    torch.cuda.synchronize()
+
+    xp64, xc64, w64 = G.host64(x_prev), G.host64(x_cur), G.host64(w)
+    kc, vc = ref.init_kv_cache(xp64, w64)
+    G.assert_bf16_close(k_init, kc, "initial K cache")
+    G.assert_bf16_close(v_init, vc, "initial V cache")
+    scores = ref.token_scores(xc64, xp64)
+    mask = ref.select_topk(scores, cfg.n_active)
+    gm = layer.mask.cpu().numpy().astype(bool)
+    flips = G.mask_mismatch_ok(gm, mask, scores, cfg.n_active)
+    print(f"  near-threshold mask flips: {flips}", flush=True)
+    assert flips == 0  # the static/moving gap leaves no token near the threshold here
+    idx, pidx = ref.compact(mask)
+    assert np.array_equal(layer.idx.cpu().numpy()[:idx.size], idx)
+    assert np.array_equal(layer.pidx.cpu().numpy()[:pidx.size], pidx)
+    assert int(layer.n_active.item()) == idx.size
+    gs = G.host64(layer.scores)
+    fin = np.isfinite(scores)
+    assert np.max(np.abs(gs[fin] - scores[fin]) / np.maximum(scores[fin], 1e-30)) <= G.SCORE_RTOL
+
+    p = ref.project(xc64[idx], w64, "kv")
+    ref.kv_cache_sync(kc, vc, idx, p["k"], p["v"])
+    gk, gv = G.host64(layer.k_cache), G.host64(layer.v_cache)
+    G.assert_bf16_close(gk, kc, "K cache")
+    G.assert_bf16_close(gv, vc, "V cache")
+    # stale rows are bit-identical to what the cache held before the step
+    assert np.array_equal(gk[pidx], k_init[pidx]) and np.array_equal(gv[pidx], v_init[pidx])
+
+    go = G.host64(layer.out)
+    assert np.all(go[pidx] == 0.0)  # inactive rows untouched (zero-initialised)
+    rows = idx if sample is None else np.sort(np.random.default_rng(seed).choice(idx.size, sample, replace=False))
+    q = ref.project(xc64[idx[rows]], w64, "q")["q"]
+    o = ref.attention(q, kc, vc, cfg.heads)
+    G.assert_close(go[idx[rows]], o, "output rows")
+    return layer
+
+
+def test_tiny_step_full_parity():
+    _step_case(configs.get_config("tiny"))
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_wan_shape_scaled_step(seed):
+    cfg = scaled(configs.get_config("wan13b"), frames=3, height=10, width=52)
+    _step_case(cfg, seed)
+
+
+def test_head_dim_64_scaled_step():
+    cfg = scaled(configs.get_config("wan13b"), frames=2, height=15, width=40, dim=512, heads=8)
+    _step_case(cfg, 0)
+
+
+def test_fused_and_unfused_paths_bit_identical():
+    t = tsa()
+    cfg = scaled(configs.get_config("wan13b"), frames=2, height=20, width=52)
+    inp = generate.step_inputs(cfg, 0)
+    outs = []
+    for fused in (True, False):
+        layer = t.PrunedAttentionLayer(cfg.n, cfg.dim, cfg.heads, G.dev(inp["w_qkv"]))
+        xp, xc = G.dev(inp["x_prev"]), G.dev(inp["x_cur"])
+        layer.init_cache(xp)
+        layer.step_topk(xc, xp, cfg.n_active, fused=fused)
+        outs.append((layer.out.clone(), layer.k_cache.clone(), layer.v_cache.clone()))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_threshold_step_zero_change_leaves_state():
+    t = tsa()
+    cfg = scaled(configs.get_config("wan13b"), frames=2, height=10, width=16)
+    inp = generate.step_inputs(cfg, 0)
+    layer = t.PrunedAttentionLayer(cfg.n, cfg.dim, cfg.heads, G.dev(inp["w_qkv"]))
+    xp = G.dev(inp["x_prev"])
+    layer.init_cache(xp)
+    layer.out.fill_(3.0)
+    k0, v0 = layer.k_cache.clone(), layer.v_cache.clone()
+    n_active = layer.step_threshold(xp.clone(), xp, tau=1e-6)
+    torch.cuda.synchronize()
+    assert n_active == 0
+    assert torch.equal(layer.k_cache, k0) and torch.equal(layer.v_cache, v0)
+    assert bool((layer.out == 3.0).all())
+
+
+def test_full_activity_is_dense_attention():
+    t = tsa()
+    cfg = scaled(configs.get_config("wan13b"), frames=2, height=10, width=26)
+    inp = generate.step_inputs(cfg, 1)
+    layer = t.PrunedAttentionLayer(cfg.n, cfg.dim, cfg.heads, G.dev(inp["w_qkv"]))
+    xp, xc = G.dev(inp["x_prev"]), G.dev(inp["x_cur"])
+    layer.init_cache(xp)
+    layer.step_topk(xc, xp, cfg.n)
+    torch.cuda.synchronize()
+    p = ref.project(G.host64(inp["x_cur"]), G.host64(inp["w_qkv"]))
+    G.assert_close(G.host64(layer.out), ref.attention(p["q"], p["k"], p["v"], cfg.heads), "dense")
+
+
+def test_hsa_schedule_loop_scaled():
+    t = tsa()
+    cfg = scaled(configs.get_config("hsa"), frames=2, height=12, width=52)
+    inp = generate.hsa_inputs(cfg, 0)
+    xs, w = inp["xs"], inp["w_qkv"]
+    counts, periods = cfg.group_counts(), cfg.group_periods()
+    assert sum(counts) == cfg.n
+    layer = t.PrunedAttentionLayer(cfg.n, cfg.dim, cfg.heads, G.dev(w))
+    xds = [G.dev(x) for x in xs]
+    layer.init_cache(xds[0])
+    # rank once at step 0 from the change between x_1 and x_0
+    layer.select(xds[1], xds[0], k=1)
+    period = torch.empty(cfg.n, dtype=torch.uint8, device="cuda")
+    t.assign_groups(layer.scores, counts, periods, period, layer.workspace)
+
+    w64 = G.host64(w)
+    x64 = [G.host64(x) for x in xs]
+    kc, vc = ref.init_kv_cache(x64[0], w64)
+    out = np.zeros((cfg.n, cfg.dim))
+    s0 = ref.token_scores(x64[1], x64[0])
+    per = ref.assign_periods(s0, counts, periods)
+    assert np.array_equal(period.cpu().numpy(), per)
+    for i in range(cfg.steps):
+        n_act = t.hsa_active_count(counts, periods, i)
+        layer.select(None, periods=period, step=i)
+        layer.forward_active(xds[i + 1], n_act)
+        torch.cuda.synchronize()
+        res = ref.layer_step(x64[i + 1], w64, cfg.heads, kc, vc, out, mask=ref.schedule_mask(per, i))
+        assert res["idx"].size == n_act
+        assert np.array_equal(layer.idx.cpu().numpy()[:n_act], res["idx"])
+        G.assert_close(G.host64(layer.out), out, f"step {i} out")
+        G.assert_bf16_close(G.host64(layer.k_cache), kc, f"step {i} K cache")
+
+
+def _lipar_case(cfg, pct_index, seed=0, sample=None):
+    t = tsa()
+    inp = generate.lipar_inputs(cfg, seed)
+    x, w = inp["x"], inp["w_qkv"]
+    eps = generate.lipar_eps(cfg, seed, pct_index)
+    k = cfg.sweep_counts()[pct_index]
+    print(f"  case {cfg.name} N={cfg.n} D={cfg.dim} k={k}", flush=True)
+    layer = t.PrunedAttentionLayer(cfg.n, cfg.dim, cfg.heads, G.dev(w))
+    xd = G.dev(x)
+    layer.step_lipar(xd, G.dev(eps), cfg.hw, k, cfg.sigma)
+    torch.cuda.synchronize()
+    x64, w64, e64 = G.host64(x), G.host64(w), G.host64(eps)
+    kc = np.zeros((cfg.n, cfg.dim))
+    vc = np.zeros((cfg.n, cfg.dim))
+    out = np.zeros((cfg.n, cfg.dim))
+    rows = None
+    if sample is not None:
+        rows = np.sort(np.random.default_rng(seed).choice(k, min(sample, k), replace=False))
+    res = ref.lipar_step(x64, e64, w64, cfg.heads, cfg.hw, k, cfg.sigma, kc, vc, out, query_rows=rows)
+    gm = layer.mask.cpu().numpy().astype(bool)
+    flips = G.mask_mismatch_ok(gm, res["mask"], res["scores"], k)
+    print(f"  near-threshold mask flips: {flips}", flush=True)
+    if flips:
+        # compare downstream with the oracle's own mask fed to the GPU (MASK mode)
+        layer.k_cache.zero_()
+        layer.v_cache.zero_()
+        layer.out.zero_()
+        mask_d = G.dev(torch.from_numpy(res["mask"].astype(np.uint8)))
+        layer.select(None, mask=mask_d)
+        from token_sparse_attention_rel_amd import _binding as B
+        B.qkv_active(xd, layer.idx, k, layer.w_qkv, q_out=layer.q_a, k_out=layer.k_cache,
+                     v_out=layer.v_cache, out_is_cache=True, n_cache=cfg.n)
+        if cfg.n - k:
+            B.qkv_active(xd, layer.pidx, cfg.n - k, layer.w_qkv, k_out=layer.k_cache,
+                         v_out=layer.v_cache, out_is_cache=True, n_cache=cfg.n, eps=G.dev(eps),
+                         src_row_offset=cfg.hw, sigma=cfg.sigma)
+        B.sparse_query_attention(layer.q_a, layer.k_cache, layer.v_cache, k, cfg.heads,
+                                 cfg.dim // cfg.heads, layer.out, out_rows=layer.idx)
+        torch.cuda.synchronize()
+    idx = res["idx"]
+    assert np.array_equal(layer.idx.cpu().numpy()[:k], idx)
+    gk, gv = G.host64(layer.k_cache), G.host64(layer.v_cache)
+    pidx = res["pidx"]
+    # rows of active tokens: same bf16 inputs as the oracle -> within one ulp
+    G.assert_bf16_close(gk[idx], kc[idx], "K cache (active rows)")
+    G.assert_bf16_close(gv[idx], vc[idx], "V cache (active rows)")
+    if pidx.size:
+        # rows from recovered inputs: those inputs carry their own fp32 rounding, so compare
+        # with the layer tolerance, max-abs taken relative to max(1, |value|)
+        for name, a, b in (("K", gk[pidx], kc[pidx]), ("V", gv[pidx], vc[pidx])):
+            rf = G.rel_frob(a, b)
+            rel_abs = float(np.max(np.abs(a - b) / np.maximum(1.0, np.abs(b))))
+            print(f"  {name} cache (recovered rows): rel_frob={rf:.3e} scaled max_abs={rel_abs:.3e}", flush=True)
+            assert rf <= G.REL_FROB and rel_abs <= G.MAX_ABS
+    go = G.host64(layer.out)
+    if rows is None:
+        G.assert_close(go[idx], res["o_a"], "output rows")
+    else:
+        G.assert_close(go[idx[rows]], res["o_a"], "sampled output rows")
+    return flips
+
+
+@pytest.mark.parametrize("pct_index", [0, 1, 2, 3, 4])
+def test_lipar_sweep_scaled(pct_index):
+    cfg = scaled(configs.get_config("lipar"), frames=5, height=9, width=16, dim=256, heads=2)
+    _lipar_case(cfg, pct_index)
+
+
+# ----------------------------------------------------------- full size
+
+@pytest.mark.slow
+def test_wan13b_full_size_sampled():
+    _step_case(configs.get_config("wan13b"), 0, sample=96)
+
+
+@pytest.mark.slow
+def test_large_full_size_sampled():
+    _step_case(configs.get_config("large"), 0, sample=48)
+
+
+@pytest.mark.slow
+def test_lipar_full_size_sampled():
+    _lipar_case(configs.get_config("lipar"), 2, sample=48)

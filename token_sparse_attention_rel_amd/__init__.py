@@ -1,0 +1,43 @@
+"""Token-pruned self-attention for MI355X (gfx950): a C-ABI HIP library plus a thin binding.
+
+The compute path is libtsa.so (include/tsa.h); this package only loads it,
+marshals arguments (``_binding``) and sequences the calls of one layer step
+(``layer``).  Importing the package loads the library and raises if it has
+not been built: there is no CPU fallback.
+"""
+
+from . import _binding
+from ._binding import (
+    BF16,
+    F32,
+    SCORE_ABS_L1,
+    SCORE_REL_L1,
+    SELECT_MASK,
+    SELECT_SCHEDULE,
+    SELECT_THRESHOLD,
+    SELECT_TOPK,
+    TsaError,
+    abi_version,
+    assign_groups,
+    gather_rows,
+    kv_cache_sync,
+    lib,
+    lib_path,
+    qkv_active,
+    scatter_out,
+    select_active,
+    select_workspace_bytes,
+    sparse_query_attention,
+    status_string,
+)
+from .layer import PrunedAttentionLayer, hsa_active_count
+
+lib()  # load now: fail loudly when the HIP library is missing
+
+__all__ = [
+    "BF16", "F32", "SCORE_ABS_L1", "SCORE_REL_L1", "SELECT_MASK", "SELECT_SCHEDULE",
+    "SELECT_THRESHOLD", "SELECT_TOPK", "TsaError", "abi_version", "assign_groups", "gather_rows",
+    "kv_cache_sync", "lib", "lib_path", "qkv_active", "scatter_out", "select_active",
+    "select_workspace_bytes", "sparse_query_attention", "status_string",
+    "PrunedAttentionLayer", "hsa_active_count",
+]

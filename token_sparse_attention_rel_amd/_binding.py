@@ -1,0 +1,205 @@
+"""ctypes binding of libtsa.so: argument marshalling only.
+
+Each function here has the name of a C entry point without its ``tsa_``
+prefix and forwards to it unchanged; all computation happens in the HIP
+kernels behind the C ABI.  Tensors are passed as device pointers (their
+``data_ptr()``); PyTorch only provides the memory and the stream.  A nonzero
+status raises :class:`TsaError`.
+
+There is no fallback: if the library is missing, loading it raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtsa.so")
+
+# Values of the C enums (include/tsa.h).
+OK = 0
+ERR_INVALID_ARG, ERR_SHAPE, ERR_DTYPE, ERR_ALIGNMENT, ERR_WORKSPACE, ERR_HIP = 1, 2, 3, 4, 5, 6
+F32, BF16 = 0, 1
+SCORE_REL_L1, SCORE_ABS_L1 = 0, 1
+SELECT_TOPK, SELECT_THRESHOLD, SELECT_MASK, SELECT_SCHEDULE = 0, 1, 2, 3
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+_f32 = ctypes.c_float
+_size = ctypes.c_size_t
+
+_SIGNATURES = {
+    "tsa_abi_version": (_int, []),
+    "tsa_status_string": (ctypes.c_char_p, [_int]),
+    "tsa_select_workspace_bytes": (_size, [_i64]),
+    "tsa_select_active": (_int, [_vp, _vp, _i64, _i64, _i64, _int, _int, _int, _i64, _f32, _vp, _i64,
+                                 _vp, _vp, _vp, _vp, _vp, _vp, _size, _vp]),
+    "tsa_assign_groups": (_int, [_vp, _i64, _int, _vp, _vp, _vp, _vp, _size, _vp]),
+    "tsa_qkv_active": (_int, [_vp, _int, _i64, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _int, _i64,
+                              _vp, _i64, _f32, _vp]),
+    "tsa_kv_cache_sync": (_int, [_vp, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _vp]),
+    "tsa_sparse_query_attention": (_int, [_vp, _vp, _vp, _i64, _i64, _int, _int, _f32, _vp, _vp,
+                                          _i64, _vp, _vp]),
+    "tsa_scatter_out": (_int, [_vp, _vp, _i64, _vp, _i64, _i64, _vp]),
+    "tsa_gather_rows": (_int, [_vp, _i64, _vp, _i64, _i64, _vp, _i64, _f32, _vp, _vp]),
+}
+
+_lib_handle = None
+
+
+class TsaError(RuntimeError):
+    def __init__(self, func: str, status: int):
+        self.status = status
+        super().__init__(f"{func}: {status_string(status)} (status {status})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libtsa.so with argument/return types set (raises if it is not built)."""
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(
+                f"{_LIB_PATH} is missing: build it with `python -m token_sparse_attention_rel_amd.build`"
+            )
+        h = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(h, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib_handle = h
+    return _lib_handle
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def status_string(status: int) -> str:
+    return lib().tsa_status_string(int(status)).decode()
+
+
+def abi_version() -> int:
+    return lib().tsa_abi_version()
+
+
+def select_workspace_bytes(n_rows: int) -> int:
+    return lib().tsa_select_workspace_bytes(int(n_rows))
+
+
+# ------------------------------------------------------------- marshalling
+
+def _ptr(t):
+    """Device pointer of a tensor (None -> NULL; ints pass through as raw addresses)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(name: str, status: int) -> None:
+    if status != OK:
+        raise TsaError(name, status)
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+# --------------------------------------------------------------- entry points
+
+def select_active(x_cur, x_ref, ref_row_offset, mode, *, k=0, tau=0.0, aux_in=None, step=0,
+                  score_kind=SCORE_REL_L1, scores_out=None, mask_out, idx_out, pidx_out=None,
+                  n_active_out, workspace=None, stream=None, n_rows=None, dim=None):
+    """a1-a3 (tsa_select_active).  x_cur/x_ref are [N, D] fp32 or bf16 device tensors."""
+    if x_cur is not None:
+        n_rows = x_cur.shape[0] if n_rows is None else n_rows
+        dim = x_cur.shape[1] if dim is None else dim
+        dt = _dtype_code(x_cur)
+    else:
+        dt = BF16
+        dim = 0 if dim is None else dim
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().tsa_select_active(
+        _ptr(x_cur), _ptr(x_ref), int(ref_row_offset), int(n_rows), int(dim), dt, int(score_kind),
+        int(mode), int(k), float(tau), _ptr(aux_in), int(step), _ptr(scores_out), _ptr(mask_out),
+        _ptr(idx_out), _ptr(pidx_out), _ptr(n_active_out), _ptr(workspace), ws_bytes, _stream(stream))
+    _check("tsa_select_active", st)
+
+
+def assign_groups(scores, group_counts, group_periods, period_out, workspace, stream=None):
+    """HSA rank groups (tsa_assign_groups); counts/periods are host sequences."""
+    n = scores.shape[0]
+    g = len(group_counts)
+    counts = (ctypes.c_int64 * g)(*[int(c) for c in group_counts])
+    periods = (ctypes.c_uint8 * g)(*[int(p) for p in group_periods])
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib().tsa_assign_groups(_ptr(scores), int(n), g, ctypes.cast(counts, _vp),
+                                 ctypes.cast(periods, _vp), _ptr(period_out), _ptr(workspace),
+                                 ws_bytes, _stream(stream))
+    _check("tsa_assign_groups", st)
+
+
+def qkv_active(x, rows, n, w_qkv, *, q_out=None, k_out, v_out, out_is_cache=False, n_cache=0,
+               eps=None, src_row_offset=0, sigma=0.0, stream=None):
+    """a4-a5 (+a6 when out_is_cache) (tsa_qkv_active)."""
+    st = lib().tsa_qkv_active(
+        _ptr(x), _dtype_code(x), int(x.shape[0]), _ptr(rows), int(n), int(x.shape[1]), _ptr(w_qkv),
+        _ptr(q_out), _ptr(k_out), _ptr(v_out), 1 if out_is_cache else 0, int(n_cache), _ptr(eps),
+        int(src_row_offset), float(sigma), _stream(stream))
+    _check("tsa_qkv_active", st)
+
+
+def kv_cache_sync(k_a, v_a, rows, n, k_cache, v_cache, stream=None):
+    """a6 (tsa_kv_cache_sync)."""
+    st = lib().tsa_kv_cache_sync(_ptr(k_a), _ptr(v_a), _ptr(rows), int(n), _ptr(k_cache),
+                                 _ptr(v_cache), int(k_cache.shape[0]), int(k_cache.shape[1]),
+                                 _stream(stream))
+    _check("tsa_kv_cache_sync", st)
+
+
+def sparse_query_attention(q, k_cache, v_cache, n_q, heads, head_dim, out, *, out_rows=None,
+                           scale=0.0, lse_out=None, stream=None):
+    """a7 (+a8 when out_rows is given) (tsa_sparse_query_attention)."""
+    n_out = out.shape[0]
+    st = lib().tsa_sparse_query_attention(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), int(n_q), int(k_cache.shape[0]), int(heads),
+        int(head_dim), float(scale), _ptr(out), _ptr(out_rows), int(n_out), _ptr(lse_out),
+        _stream(stream))
+    _check("tsa_sparse_query_attention", st)
+
+
+def scatter_out(o_a, rows, n, out, stream=None):
+    """a8 (tsa_scatter_out)."""
+    st = lib().tsa_scatter_out(_ptr(o_a), _ptr(rows), int(n), _ptr(out), int(out.shape[0]),
+                               int(out.shape[1]), _stream(stream))
+    _check("tsa_scatter_out", st)
+
+
+def gather_rows(x, rows, n, dst, *, eps=None, src_row_offset=0, sigma=0.0, stream=None):
+    """a4 alone (tsa_gather_rows)."""
+    st = lib().tsa_gather_rows(_ptr(x), int(x.shape[0]), _ptr(rows), int(n), int(x.shape[1]),
+                               _ptr(eps), int(src_row_offset), float(sigma), _ptr(dst),
+                               _stream(stream))
+    _check("tsa_gather_rows", st)

@@ -1,0 +1,77 @@
+// Device helpers shared by the tsa kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tsa {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// bf16 bits -> fp32 (exact).
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 b = static_cast<__bf16>(f);
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+// Two fp32 -> packed bf16 pair (low half = a).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+}
+
+// Unpack 8 bf16 held in a 16-byte vector into fp32.
+__device__ __forceinline__ void unpack8(const u32x4 v, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(v[i] << 16);
+    f[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+  }
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+// Number of set lanes of a 64-bit ballot below the calling lane.
+__device__ __forceinline__ int lanes_below(uint64_t ballot) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(ballot >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(ballot), 0));
+}
+
+}  // namespace tsa
+
+namespace tsa {
+
+// Workgroups of a 1-D grid are dispatched round-robin over the 8 XCDs of the
+// chip (block b runs on XCD b % 8).  Remap block ids so that each XCD works on
+// one contiguous range of logical tiles: tiles that share inputs (e.g. the
+// query tiles of one head, which all stream that head's K/V) then share the
+// XCD's L2.  The mapping is a bijection on [0, total).
+__device__ __forceinline__ long xcd_remap(long b, long total) {
+  constexpr long kXcd = 8;
+  const long q = total / kXcd, r = total % kXcd;
+  const long xcd = b % kXcd, slot = b / kXcd;
+  return xcd * q + (xcd < r ? xcd : r) + slot;
+}
+
+}  // namespace tsa

@@ -1,0 +1,56 @@
+// Host-side launchers of the tsa kernels (one per .hip file), called by the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tsa {
+
+// Mirrors of the public enums (include/tsa.h) used inside the kernels.
+enum { kDtypeF32 = 0, kDtypeBf16 = 1 };
+enum { kSelectTopk = 0, kSelectThreshold = 1, kSelectMask = 2, kSelectSchedule = 3 };
+
+struct GroupPeriods {
+  uint8_t p[16];
+};
+
+// select.hip
+hipError_t launch_scores(const void* x_cur, const void* x_ref, long ref_off, long n_rows,
+                         long dim, int dtype, int relative, float* scores, hipStream_t s);
+hipError_t launch_select(const float* scores, const uint8_t* aux, int n, int mode, int k,
+                         float tau, long step, uint8_t* mask, int* idx, int* pidx, int* n_active,
+                         uint8_t* group_accum, int accum_first, hipStream_t s);
+hipError_t launch_map_groups(const uint8_t* group, int n, const GroupPeriods& table,
+                             uint8_t* period_out, hipStream_t s);
+
+// rowops.hip
+struct RowSource {
+  const void* x;        // token rows [n_x_rows, dim]
+  int x_dtype;          // kDtypeF32 / kDtypeBf16
+  long n_x_rows;
+  const int* rows;      // token of row r, or nullptr for r
+  const uint16_t* eps;  // recovery noise [n_x_rows, dim] or nullptr
+  long src_off;         // recovery: clean row of token t is x[t - src_off]
+  float sigma;
+};
+hipError_t launch_gather_rows(const RowSource& src, long n, long dim, uint16_t* dst,
+                              hipStream_t s);
+hipError_t launch_copy_rows2(const uint16_t* a, const uint16_t* b, const int* rows, long n,
+                             uint16_t* da, uint16_t* db, long dim, hipStream_t s);
+
+// qkv_gemm.hip
+struct QkvOut {
+  uint16_t* q;      // [n, dim] or nullptr
+  uint16_t* k;      // compact [n, dim] or cache [n_cache, dim]
+  uint16_t* v;
+  int to_cache;     // k/v row r goes to row rows[r]
+};
+hipError_t launch_qkv(const RowSource& src, long n, long dim, const uint16_t* w_qkv,
+                      const QkvOut& out, hipStream_t s);
+
+// attention.hip
+hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, long n_q,
+                            long n_kv, int heads, int head_dim, float scale, uint16_t* out,
+                            const int* out_rows, float* lse, hipStream_t s);
+
+}  // namespace tsa

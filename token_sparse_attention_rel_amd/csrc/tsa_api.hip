@@ -1,0 +1,206 @@
+// C ABI of libtsa: argument validation, then kernel launches on the caller's stream.
+//
+// Every entry point validates all arguments before enqueuing anything, so a
+// rejected call writes nothing.  Nothing here allocates, frees or
+// synchronises; nothing keeps state between calls.
+#include <math.h>
+
+#include "../../include/tsa.h"
+#include "kernels.h"
+
+namespace {
+
+using tsa::RowSource;
+
+constexpr int64_t kMaxRows = (int64_t{1} << 31) - 1;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+tsa_status from_hip(hipError_t e) { return e == hipSuccess ? TSA_OK : TSA_ERR_HIP; }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int tsa_abi_version(void) { return TSA_ABI_VERSION; }
+
+const char* tsa_status_string(int status) {
+  switch (status) {
+    case TSA_OK: return "ok";
+    case TSA_ERR_INVALID_ARG: return "invalid argument";
+    case TSA_ERR_SHAPE: return "invalid shape";
+    case TSA_ERR_DTYPE: return "unsupported dtype";
+    case TSA_ERR_ALIGNMENT: return "buffer not 16-byte aligned";
+    case TSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case TSA_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t tsa_select_workspace_bytes(int64_t n_rows) {
+  (void)n_rows;
+  return 0;
+}
+
+tsa_status tsa_select_active(const void* x_cur, const void* x_ref, int64_t ref_row_offset,
+                             int64_t n_rows, int64_t dim, int dtype, int score_kind, int mode,
+                             int64_t k, float tau, const uint8_t* aux_in, int64_t step,
+                             float* scores_out, uint8_t* mask_out, int32_t* idx_out,
+                             int32_t* pidx_out, int32_t* n_active_out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  if (mode < TSA_SELECT_TOPK || mode > TSA_SELECT_SCHEDULE) return TSA_ERR_INVALID_ARG;
+  if (score_kind != TSA_SCORE_REL_L1 && score_kind != TSA_SCORE_ABS_L1) return TSA_ERR_INVALID_ARG;
+  if (n_rows < 0 || n_rows > kMaxRows) return TSA_ERR_SHAPE;
+  const bool scored = mode == TSA_SELECT_TOPK || mode == TSA_SELECT_THRESHOLD;
+  if (!mask_out || !idx_out || !n_active_out) return TSA_ERR_INVALID_ARG;
+  if (scored) {
+    if (dtype != TSA_F32 && dtype != TSA_BF16) return TSA_ERR_DTYPE;
+    if (!x_cur || !scores_out) return TSA_ERR_INVALID_ARG;
+    if (dim <= 0 || dim % 8 != 0) return TSA_ERR_SHAPE;
+    if (!aligned16(x_cur) || (x_ref && !aligned16(x_ref)) || !aligned16(scores_out))
+      return TSA_ERR_ALIGNMENT;
+    if (mode == TSA_SELECT_TOPK && (k < 0 || k > n_rows)) return TSA_ERR_SHAPE;
+    if (mode == TSA_SELECT_THRESHOLD && isnan(tau)) return TSA_ERR_INVALID_ARG;
+  } else {
+    if (!aux_in) return TSA_ERR_INVALID_ARG;
+    if (mode == TSA_SELECT_SCHEDULE && step < 0) return TSA_ERR_SHAPE;
+  }
+  if (!aligned4(idx_out) || (pidx_out && !aligned4(pidx_out)) || !aligned4(n_active_out))
+    return TSA_ERR_ALIGNMENT;
+  if (workspace_bytes < tsa_select_workspace_bytes(n_rows)) return TSA_ERR_WORKSPACE;
+  if (n_rows == 0) return TSA_OK;
+
+  hipStream_t s = as_stream(stream);
+  if (scored) {
+    hipError_t e = tsa::launch_scores(x_cur, x_ref, ref_row_offset, n_rows, dim, dtype,
+                                      score_kind == TSA_SCORE_REL_L1, scores_out, s);
+    if (e != hipSuccess) return TSA_ERR_HIP;
+  }
+  return from_hip(tsa::launch_select(scores_out, aux_in, static_cast<int>(n_rows), mode,
+                                     static_cast<int>(k), tau, step, mask_out, idx_out, pidx_out,
+                                     n_active_out, nullptr, 0, s));
+}
+
+tsa_status tsa_assign_groups(const float* scores, int64_t n, int n_groups,
+                             const int64_t* group_counts, const uint8_t* group_periods,
+                             uint8_t* period_out, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  if (!scores || !group_counts || !group_periods || !period_out) return TSA_ERR_INVALID_ARG;
+  if (n < 0 || n > kMaxRows) return TSA_ERR_SHAPE;
+  if (n_groups < 1 || n_groups > 16) return TSA_ERR_SHAPE;
+  int64_t total = 0;
+  for (int g = 0; g < n_groups; ++g) {
+    if (group_counts[g] < 0) return TSA_ERR_SHAPE;
+    total += group_counts[g];
+  }
+  if (total != n) return TSA_ERR_SHAPE;
+  if (!aligned16(scores)) return TSA_ERR_ALIGNMENT;
+  const size_t need = tsa_select_workspace_bytes(n) + static_cast<size_t>(n);
+  if (n > 0 && (!workspace || workspace_bytes < need)) return TSA_ERR_WORKSPACE;
+  if (n == 0) return TSA_OK;
+
+  hipStream_t s = as_stream(stream);
+  uint8_t* group = static_cast<uint8_t*>(workspace) + tsa_select_workspace_bytes(n);
+  // Group of a token = number of rank boundaries it falls behind; the top-c
+  // sets for increasing cumulative counts c are nested (one total order).
+  int64_t cum = 0;
+  for (int g = 0; g + 1 < n_groups; ++g) {
+    cum += group_counts[g];
+    hipError_t e = tsa::launch_select(scores, nullptr, static_cast<int>(n), TSA_SELECT_TOPK,
+                                      static_cast<int>(cum), 0.f, 0, nullptr, nullptr, nullptr,
+                                      nullptr, group, g == 0, s);
+    if (e != hipSuccess) return TSA_ERR_HIP;
+  }
+  tsa::GroupPeriods table{};
+  for (int g = 0; g < n_groups; ++g) table.p[g] = group_periods[g];
+  return from_hip(tsa::launch_map_groups(n_groups > 1 ? group : nullptr, static_cast<int>(n), table,
+                                         period_out, s));
+}
+
+tsa_status tsa_qkv_active(const void* x, int x_dtype, int64_t n_x_rows, const int32_t* rows,
+                          int64_t n, int64_t dim, const tsa_bf16* w_qkv, tsa_bf16* q_out,
+                          tsa_bf16* k_out, tsa_bf16* v_out, int out_is_cache, int64_t n_cache,
+                          const tsa_bf16* eps, int64_t src_row_offset, float sigma,
+                          void* stream) {
+  if (!x || !w_qkv || !k_out || !v_out) return TSA_ERR_INVALID_ARG;
+  if (x_dtype != TSA_F32 && x_dtype != TSA_BF16) return TSA_ERR_DTYPE;
+  if (eps && x_dtype != TSA_BF16) return TSA_ERR_DTYPE;
+  if (out_is_cache && !rows) return TSA_ERR_INVALID_ARG;
+  if (eps && isnan(sigma)) return TSA_ERR_INVALID_ARG;
+  if (n < 0 || n > kMaxRows || n_x_rows < 0 || n_x_rows > kMaxRows) return TSA_ERR_SHAPE;
+  if (dim <= 0 || dim % 64 != 0 || dim > (int64_t{1} << 20)) return TSA_ERR_SHAPE;
+  if (!rows && n > n_x_rows) return TSA_ERR_SHAPE;
+  if (out_is_cache && (n_cache < 0 || n_cache > kMaxRows)) return TSA_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(w_qkv) || (q_out && !aligned16(q_out)) || !aligned16(k_out) ||
+      !aligned16(v_out) || (eps && !aligned16(eps)) || (rows && !aligned4(rows)))
+    return TSA_ERR_ALIGNMENT;
+  if (n == 0) return TSA_OK;
+  RowSource src{x, x_dtype, n_x_rows, rows, eps, src_row_offset, sigma};
+  tsa::QkvOut out{q_out, k_out, v_out, out_is_cache ? 1 : 0};
+  return from_hip(tsa::launch_qkv(src, n, dim, w_qkv, out, as_stream(stream)));
+}
+
+tsa_status tsa_kv_cache_sync(const tsa_bf16* k_a, const tsa_bf16* v_a, const int32_t* rows,
+                             int64_t n, tsa_bf16* k_cache, tsa_bf16* v_cache, int64_t n_cache,
+                             int64_t dim, void* stream) {
+  if (!k_a || !v_a || !rows || !k_cache || !v_cache) return TSA_ERR_INVALID_ARG;
+  if (n < 0 || n > kMaxRows || n_cache < 0 || n_cache > kMaxRows) return TSA_ERR_SHAPE;
+  if (n > n_cache || dim <= 0 || dim % 8 != 0) return TSA_ERR_SHAPE;
+  if (!aligned16(k_a) || !aligned16(v_a) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      !aligned4(rows))
+    return TSA_ERR_ALIGNMENT;
+  if (n == 0) return TSA_OK;
+  return from_hip(tsa::launch_copy_rows2(k_a, v_a, rows, n, k_cache, v_cache, dim,
+                                         as_stream(stream)));
+}
+
+tsa_status tsa_sparse_query_attention(const tsa_bf16* q, const tsa_bf16* k_cache,
+                                      const tsa_bf16* v_cache, int64_t n_q, int64_t n_kv,
+                                      int heads, int head_dim, float scale, tsa_bf16* out,
+                                      const int32_t* out_rows, int64_t n_out, float* lse_out,
+                                      void* stream) {
+  if (!q || !k_cache || !v_cache || !out) return TSA_ERR_INVALID_ARG;
+  if (isnan(scale) || isinf(scale)) return TSA_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128) return TSA_ERR_SHAPE;
+  if (heads < 1 || heads > 4096) return TSA_ERR_SHAPE;
+  if (n_q < 0 || n_q > kMaxRows || n_kv < 1 || n_kv > kMaxRows) return TSA_ERR_SHAPE;
+  if (out_rows && (n_out < 0 || n_out > kMaxRows)) return TSA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+      (out_rows && !aligned4(out_rows)) || (lse_out && !aligned4(lse_out)))
+    return TSA_ERR_ALIGNMENT;
+  if (n_q == 0) return TSA_OK;
+  const float sc = scale > 0.f ? scale : 1.0f / sqrtf(static_cast<float>(head_dim));
+  return from_hip(tsa::launch_attention(q, k_cache, v_cache, n_q, n_kv, heads, head_dim, sc, out,
+                                        out_rows, lse_out, as_stream(stream)));
+}
+
+tsa_status tsa_scatter_out(const tsa_bf16* o_a, const int32_t* rows, int64_t n, tsa_bf16* out,
+                           int64_t n_out, int64_t dim, void* stream) {
+  if (!o_a || !rows || !out) return TSA_ERR_INVALID_ARG;
+  if (n < 0 || n > kMaxRows || n_out < 0 || n_out > kMaxRows) return TSA_ERR_SHAPE;
+  if (n > n_out || dim <= 0 || dim % 8 != 0) return TSA_ERR_SHAPE;
+  if (!aligned16(o_a) || !aligned16(out) || !aligned4(rows)) return TSA_ERR_ALIGNMENT;
+  if (n == 0) return TSA_OK;
+  return from_hip(
+      tsa::launch_copy_rows2(o_a, nullptr, rows, n, out, nullptr, dim, as_stream(stream)));
+}
+
+tsa_status tsa_gather_rows(const tsa_bf16* x, int64_t n_x_rows, const int32_t* rows, int64_t n,
+                           int64_t dim, const tsa_bf16* eps, int64_t src_row_offset, float sigma,
+                           tsa_bf16* dst, void* stream) {
+  if (!x || !rows || !dst) return TSA_ERR_INVALID_ARG;
+  if (eps && isnan(sigma)) return TSA_ERR_INVALID_ARG;
+  if (n < 0 || n > kMaxRows || n_x_rows < 0 || n_x_rows > kMaxRows) return TSA_ERR_SHAPE;
+  if (dim <= 0 || dim % 8 != 0) return TSA_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(dst) || (eps && !aligned16(eps)) || !aligned4(rows))
+    return TSA_ERR_ALIGNMENT;
+  if (n == 0) return TSA_OK;
+  RowSource src{x, TSA_BF16, n_x_rows, rows, eps, src_row_offset, sigma};
+  return from_hip(tsa::launch_gather_rows(src, n, dim, dst, as_stream(stream)));
+}
+
+}  // extern "C"

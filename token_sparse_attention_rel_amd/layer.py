@@ -1,0 +1,130 @@
+"""Driver of one pruned attention layer on one GPU: owns the persistent buffers
+and sequences the C-ABI calls.  No arithmetic happens here.
+
+A step (HSA page §2.2) is: score + select + compact (select_active), QKV of
+the active tokens with their K/V written straight into the cache rows
+(qkv_active with the cache sync fused), attention of the active queries over
+the whole cache with the outputs written straight to their token rows
+(sparse_query_attention with the scatter fused).  ``fused=False`` runs the
+same step with the standalone cache-sync and scatter kernels instead.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import _binding as B
+
+
+class PrunedAttentionLayer:
+    def __init__(self, n: int, dim: int, heads: int, w_qkv: torch.Tensor, device="cuda"):
+        if dim % heads:
+            raise ValueError("dim must be a multiple of heads")
+        self.n, self.dim, self.heads = n, dim, heads
+        self.head_dim = dim // heads
+        self.device = torch.device(device)
+        dev = self.device
+        self.w_qkv = w_qkv.to(dev, torch.bfloat16).contiguous()
+        bf = torch.bfloat16
+        # persistent state: the per-layer KV cache and the output in token order
+        self.k_cache = torch.zeros(n, dim, dtype=bf, device=dev)
+        self.v_cache = torch.zeros(n, dim, dtype=bf, device=dev)
+        self.out = torch.zeros(n, dim, dtype=bf, device=dev)
+        # per-step scratch
+        self.scores = torch.empty(n, dtype=torch.float32, device=dev)
+        self.mask = torch.empty(n, dtype=torch.uint8, device=dev)
+        self.idx = torch.empty(n, dtype=torch.int32, device=dev)
+        self.pidx = torch.empty(n, dtype=torch.int32, device=dev)
+        self.n_active = torch.empty(1, dtype=torch.int32, device=dev)
+        self.q_a = torch.empty(n, dim, dtype=bf, device=dev)
+        self._k_a = None
+        self._v_a = None
+        self._o_a = None
+        ws = B.select_workspace_bytes(n)
+        self.workspace = torch.empty(max(ws, 16) + n, dtype=torch.uint8, device=dev)
+
+    # ---------------------------------------------------------------- state
+
+    def init_cache(self, x_prev: torch.Tensor, stream=None) -> None:
+        """K/V cache = projections of every token of x_prev (the start of a run)."""
+        B.qkv_active(x_prev, None, self.n, self.w_qkv, q_out=None, k_out=self.k_cache,
+                     v_out=self.v_cache, stream=stream)
+
+    def _compact_bufs(self):
+        if self._k_a is None:
+            bf = torch.bfloat16
+            self._k_a = torch.empty(self.n, self.dim, dtype=bf, device=self.device)
+            self._v_a = torch.empty(self.n, self.dim, dtype=bf, device=self.device)
+            self._o_a = torch.empty(self.n, self.dim, dtype=bf, device=self.device)
+        return self._k_a, self._v_a, self._o_a
+
+    # ---------------------------------------------------------------- steps
+
+    def select(self, x_cur, x_ref=None, *, k=None, tau=None, mask=None, periods=None, step=0,
+               ref_row_offset=0, score_kind=B.SCORE_REL_L1, stream=None) -> None:
+        if mask is not None:
+            B.select_active(None, None, 0, B.SELECT_MASK, aux_in=mask, mask_out=self.mask,
+                            idx_out=self.idx, pidx_out=self.pidx, n_active_out=self.n_active,
+                            n_rows=self.n, stream=stream)
+        elif periods is not None:
+            B.select_active(None, None, 0, B.SELECT_SCHEDULE, aux_in=periods, step=step,
+                            mask_out=self.mask, idx_out=self.idx, pidx_out=self.pidx,
+                            n_active_out=self.n_active, n_rows=self.n, stream=stream)
+        else:
+            mode = B.SELECT_TOPK if k is not None else B.SELECT_THRESHOLD
+            B.select_active(x_cur, x_ref, ref_row_offset, mode, k=k or 0,
+                            tau=0.0 if tau is None else tau, score_kind=score_kind,
+                            scores_out=self.scores, mask_out=self.mask, idx_out=self.idx,
+                            pidx_out=self.pidx, n_active_out=self.n_active, stream=stream)
+
+    def forward_active(self, x_cur, n_active: int, *, fused=True, stream=None) -> None:
+        """QKV of the selected tokens, cache sync, attention, scatter (after select)."""
+        if n_active == 0:
+            return
+        idx = self.idx
+        if fused:
+            B.qkv_active(x_cur, idx, n_active, self.w_qkv, q_out=self.q_a, k_out=self.k_cache,
+                         v_out=self.v_cache, out_is_cache=True, n_cache=self.n, stream=stream)
+            B.sparse_query_attention(self.q_a, self.k_cache, self.v_cache, n_active, self.heads,
+                                     self.head_dim, self.out, out_rows=idx, stream=stream)
+        else:
+            k_a, v_a, o_a = self._compact_bufs()
+            B.qkv_active(x_cur, idx, n_active, self.w_qkv, q_out=self.q_a, k_out=k_a, v_out=v_a,
+                         stream=stream)
+            B.kv_cache_sync(k_a, v_a, idx, n_active, self.k_cache, self.v_cache, stream=stream)
+            B.sparse_query_attention(self.q_a, self.k_cache, self.v_cache, n_active, self.heads,
+                                     self.head_dim, o_a, stream=stream)
+            B.scatter_out(o_a, idx, n_active, self.out, stream=stream)
+
+    def step_topk(self, x_cur, x_ref, k: int, *, fused=True, stream=None) -> None:
+        """One step with a fixed active count k (no host synchronisation)."""
+        self.select(x_cur, x_ref, k=k, stream=stream)
+        self.forward_active(x_cur, k, fused=fused, stream=stream)
+
+    def step_threshold(self, x_cur, x_ref, tau: float, *, fused=True, stream=None) -> int:
+        """One step with s >= tau active; reads the active count back (one synchronisation)."""
+        self.select(x_cur, x_ref, tau=tau, stream=stream)
+        n_active = int(self.n_active.item())
+        self.forward_active(x_cur, n_active, fused=fused, stream=stream)
+        return n_active
+
+    def step_lipar(self, x, eps, hw: int, k: int, sigma: float, *, stream=None) -> None:
+        """Inter-frame pass over a whole clip (LIPAR page §2.B-§2.C): score each token against
+        the same location one frame earlier, keep the top k, project active tokens from their
+        latent and pruned tokens from the recovered row, attend, scatter."""
+        self.select(x, None, k=k, ref_row_offset=hw, stream=stream)
+        B.qkv_active(x, self.idx, k, self.w_qkv, q_out=self.q_a, k_out=self.k_cache,
+                     v_out=self.v_cache, out_is_cache=True, n_cache=self.n, stream=stream)
+        n_p = self.n - k
+        if n_p:
+            B.qkv_active(x, self.pidx, n_p, self.w_qkv, q_out=None, k_out=self.k_cache,
+                         v_out=self.v_cache, out_is_cache=True, n_cache=self.n, eps=eps,
+                         src_row_offset=hw, sigma=sigma, stream=stream)
+        if k:
+            B.sparse_query_attention(self.q_a, self.k_cache, self.v_cache, k, self.heads,
+                                     self.head_dim, self.out, out_rows=self.idx, stream=stream)
+
+
+def hsa_active_count(group_counts, group_periods, step: int) -> int:
+    """Active tokens at a global step of the HSA schedule (known on the host)."""
+    return sum(c for c, p in zip(group_counts, group_periods) if p and step % p == 0)
