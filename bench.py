@@ -41,7 +41,24 @@ def parse_args(argv=None):
     ap.add_argument("--cpu-sample-rows", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy 5 times (HBM counter calibration)")
     return ap.parse_args(argv)
+
+
+def copy_calibration():
+    """A plain device-to-device copy of known size, to calibrate the HBM byte counters:
+    each launch reads and writes exactly 2**30 bytes."""
+    import torch
+
+    a = torch.ones(2 ** 29, dtype=torch.bfloat16, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read_per_launch": 2 ** 30,
+                      "copy_calibration_bytes_written_per_launch": 2 ** 30}), flush=True)
+    return 0
 
 
 def _src_hash(path):
@@ -119,6 +136,9 @@ def main(argv=None):
         print("bench.py measures one GPU only: the pruned layer runs unsharded on a single MI355X "
               "(multi-GPU sharding is design-only). Run with --gpus 1.", file=sys.stderr)
         return 2
+
+    if args.copy_calibration:
+        return copy_calibration()
 
     import torch
 

@@ -91,3 +91,25 @@ def assert_bf16_close(got, want, what=""):
     print(f"  {what}: rel_frob={rf:.3e}, {int((d == 1).sum())} of {d.size} one-ulp differences, "
           f"max {int(d.max()) if d.size else 0} ulp", flush=True)
     assert rf <= REL_FROB and (d.size == 0 or d.max() <= 1), what
+
+
+def bf16_ulp_of(v) -> np.ndarray:
+    """Spacing of bf16 numbers at |v| (2**(e-7) for |v| in [2**e, 2**(e+1)))."""
+    a = np.maximum(np.abs(np.asarray(v, np.float64)), 2.0 ** -126)
+    return np.exp2(np.floor(np.log2(a)) - 7)
+
+
+def assert_projection_close(got, want, abs_dot, k_terms, what=""):
+    """bf16 results of a length-k dot product accumulated in fp32, against the oracle's
+    bf16 rounding of the exact value:  |got - want| <= ulp(got)/2 + ulp(want)/2 + k * 2**-24 * sum|x||w|
+    (two roundings to bf16 plus the classic bound on fp32 summation error), elementwise;
+    plus the relative Frobenius bound of the layer."""
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    bound = 0.5 * (bf16_ulp_of(got) + bf16_ulp_of(want)) + k_terms * 2.0 ** -24 * np.asarray(abs_dot)
+    err = np.abs(got - want)
+    rf = rel_frob(got, want)
+    d = ulp_distance(got, want)
+    print(f"  {what}: rel_frob={rf:.3e}, {int((d > 0).sum())} of {d.size} differ, "
+          f"max err/bound {float(np.max(err / bound)) if err.size else 0:.3f}", flush=True)
+    assert rf <= REL_FROB and np.all(err <= bound), what

@@ -292,7 +292,10 @@ def test_qkv_matches_oracle(n_x, m, dim, src):
             # the recovered input rows carry their own fp32 rounding (see the gather test)
             G.assert_close(gh, want[name], f"{src} {name}")
         else:
-            G.assert_bf16_close(gh, want[name], f"{src} {name}")
+            part = "qkv".index(name)
+            wp = np.abs(G.host64(w)[part * dim:(part + 1) * dim])
+            G.assert_projection_close(gh, want[name], np.abs(ref.round_bf16(a_rows)) @ wp.T, dim,
+                                      f"{src} {name}")
     # K/V only, written into cache rows (fused cache sync); other rows untouched
     kc = _randn_bf16(g, n_x, dim)
     vc = _randn_bf16(g, n_x, dim)

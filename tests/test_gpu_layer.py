@@ -46,8 +46,14 @@ def _step_case(cfg, seed=0, fused=True, sample=None):
 
     xp64, xc64, w64 = G.host64(x_prev), G.host64(x_cur), G.host64(w)
     kc, vc = ref.init_kv_cache(xp64, w64)
-    G.assert_bf16_close(k_init, kc, "initial K cache")
-    G.assert_bf16_close(v_init, vc, "initial V cache")
+    d = cfg.dim
+    # elementwise bound on a seeded sample of rows (all rows for the small workloads)
+    chk = np.arange(cfg.n) if cfg.n <= 40000 else np.sort(np.random.default_rng(7).choice(cfg.n, 4096, replace=False))
+    axp = np.abs(ref.round_bf16(xp64[chk]))
+    wk, wv = np.abs(w64[d:2 * d]), np.abs(w64[2 * d:])
+    G.assert_projection_close(k_init[chk], kc[chk], axp @ wk.T, d, "initial K cache")
+    G.assert_projection_close(v_init[chk], vc[chk], axp @ wv.T, d, "initial V cache")
+    G.assert_close(k_init, kc, "initial K cache (all rows)", mabs=np.inf)
     scores = ref.token_scores(xc64, xp64)
     mask = ref.select_topk(scores, cfg.n_active)
     gm = layer.mask.cpu().numpy().astype(bool)
@@ -65,14 +71,19 @@ def _step_case(cfg, seed=0, fused=True, sample=None):
     p = ref.project(xc64[idx], w64, "kv")
     ref.kv_cache_sync(kc, vc, idx, p["k"], p["v"])
     gk, gv = G.host64(layer.k_cache), G.host64(layer.v_cache)
-    G.assert_bf16_close(gk, kc, "K cache")
-    G.assert_bf16_close(gv, vc, "V cache")
+    # fresh rows: elementwise bound (sampled for the large workloads)
+    fr = idx if idx.size <= 20000 else np.sort(np.random.default_rng(8).choice(idx, 4096, replace=False))
+    axc = np.abs(ref.round_bf16(xc64[fr]))
+    G.assert_projection_close(gk[fr], kc[fr], axc @ wk.T, d, "K cache (fresh rows)")
+    G.assert_projection_close(gv[fr], vc[fr], axc @ wv.T, d, "V cache (fresh rows)")
+    G.assert_close(gk, kc, "K cache (all rows)", mabs=np.inf)
+    G.assert_close(gv, vc, "V cache (all rows)", mabs=np.inf)
     # stale rows are bit-identical to what the cache held before the step
     assert np.array_equal(gk[pidx], k_init[pidx]) and np.array_equal(gv[pidx], v_init[pidx])
 
     go = G.host64(layer.out)
     assert np.all(go[pidx] == 0.0)  # inactive rows untouched (zero-initialised)
-    rows = idx if sample is None else np.sort(np.random.default_rng(seed).choice(idx.size, sample, replace=False))
+    rows = np.arange(idx.size) if sample is None else np.sort(np.random.default_rng(seed).choice(idx.size, sample, replace=False))
     q = ref.project(xc64[idx[rows]], w64, "q")["q"]
     o = ref.attention(q, kc, vc, cfg.heads)
     G.assert_close(go[idx[rows]], o, "output rows")
@@ -169,7 +180,11 @@ def test_hsa_schedule_loop_scaled():
         assert res["idx"].size == n_act
         assert np.array_equal(layer.idx.cpu().numpy()[:n_act], res["idx"])
         G.assert_close(G.host64(layer.out), out, f"step {i} out")
-        G.assert_bf16_close(G.host64(layer.k_cache), kc, f"step {i} K cache")
+        G.assert_close(G.host64(layer.k_cache), kc, f"step {i} K cache", mabs=np.inf)
+        fresh = res["idx"]
+        ax = np.abs(x64[i + 1][fresh])
+        G.assert_projection_close(G.host64(layer.k_cache)[fresh], kc[fresh],
+                                  ax @ np.abs(w64[cfg.dim:2 * cfg.dim]).T, cfg.dim, f"step {i} fresh K")
 
 
 def _lipar_case(cfg, pct_index, seed=0, sample=None):
@@ -215,9 +230,12 @@ def _lipar_case(cfg, pct_index, seed=0, sample=None):
     assert np.array_equal(layer.idx.cpu().numpy()[:k], idx)
     gk, gv = G.host64(layer.k_cache), G.host64(layer.v_cache)
     pidx = res["pidx"]
-    # rows of active tokens: same bf16 inputs as the oracle -> within one ulp
-    G.assert_bf16_close(gk[idx], kc[idx], "K cache (active rows)")
-    G.assert_bf16_close(gv[idx], vc[idx], "V cache (active rows)")
+    # rows of active tokens: same bf16 inputs as the oracle -> rounding + fp32 summation bound
+    sm = idx if idx.size <= 20000 else np.sort(np.random.default_rng(9).choice(idx, 4096, replace=False))
+    ax = np.abs(x64[sm])
+    d = cfg.dim
+    G.assert_projection_close(gk[sm], kc[sm], ax @ np.abs(w64[d:2 * d]).T, d, "K cache (active rows)")
+    G.assert_projection_close(gv[sm], vc[sm], ax @ np.abs(w64[2 * d:]).T, d, "V cache (active rows)")
     if pidx.size:
         # rows from recovered inputs: those inputs carry their own fp32 rounding, so compare
         # with the layer tolerance, max-abs taken relative to max(1, |value|)
