@@ -7,8 +7,9 @@
 //
 // Flash-style single pass with an online softmax, bf16 MFMA, fp32 state.
 // A workgroup of 4 waves owns 128 queries of one head; each wave owns 32.
-// Key/value tiles of 64 rows are staged through LDS (K row-major, V
-// transposed) and double-buffered through registers.
+// Key/value tiles of 64 rows are staged row-major through two LDS buffers
+// (one barrier per tile); the next tile's global loads are in flight while
+// the current one is computed.
 //
 // Layout trick: the score tile is computed transposed, S^T = K Q^T, with
 // v_mfma_f32_32x32x16_bf16.  In that instruction's accumulator layout a lane
@@ -16,10 +17,9 @@
 // the rescale factor of a query all live in one lane (plus its partner lane
 // +-32, reached with a single cross-lane exchange per tile).  The output is
 // accumulated transposed too, O^T = V^T P^T: the probabilities a lane holds
-// are exactly the B operand it must supply, provided the key order inside
-// each 16-key chunk is permuted consistently -- which the transposed V
-// store into LDS does (bits 2 and 3 of the key offset swapped).  No
-// probabilities travel through LDS.
+// are exactly the B operand it must supply, provided the V^T operand uses
+// the same key order inside each 16-key chunk -- which the transposing LDS
+// reads of row-major V deliver directly.  No probabilities travel through LDS.
 #include "common.h"
 #include "kernels.h"
 
@@ -41,31 +41,34 @@ struct AttnArgs {
   float* lse;
 };
 
-// Key offset within a 16-key chunk -> LDS position (swap bits 2 and 3).
-__device__ __forceinline__ int vt_pos(int key) {
-  return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
-}
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-// Element e (0..7) of two 8 x bf16 vectors, packed as (a_e, b_e).
-__device__ __forceinline__ uint32_t pair16(const u32x4 a, const u32x4 b, int e) {
-  const uint32_t wa = a[e >> 1], wb = b[e >> 1];
-  return (e & 1) ? ((wa >> 16) | (wb & 0xffff0000u)) : ((wa & 0xffffu) | (wb << 16));
+// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane i
+// receives element i%4 of the 4-element pieces addressed by lanes i/4, 4+i/4,
+// 8+i/4 and 12+i/4.  With lane j of the group pointing at
+// V[key0 + j/4][dim0 + 4*(j%4)], lane i ends up with V[key0 + 0..3][dim0 + i]:
+// four consecutive keys of one dimension -- a column of V, as the MFMA needs.
+// `p` must point into a __shared__ array; the cast is an address-space cast.
+__device__ __forceinline__ v4i16 ds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)const_cast<uint16_t*>(p));
 }
 
 template <int HD>
 __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   constexpr int BN = kAttnBN;
-  constexpr int LDK = HD + 8;               // K row stride in LDS (elements)
-  constexpr int LDV = BN + 8;               // V^T row stride in LDS (elements)
-  constexpr int NM = HD / 16;               // MFMA steps over the head dim
-  constexpr int NDB = HD / 32;              // 32-wide output dim blocks
-  constexpr int CPR = HD / 8;               // 16-byte chunks per K/V row
-  constexpr int KCH = BN * CPR / 256;       // K chunks per thread
-  constexpr int KPT = BN * HD / 8 / 256;    // V keys per thread (8 dims each)
-  static_assert(KPT == 2 || KPT == 4, "unsupported head dim");
+  // K rows: stride HD+8 elements (16-byte reads down a column hit distinct banks).
+  // V rows: stride HD+32 elements = 64 mod 256 bytes, so the four rows touched by
+  // a 32-lane half of a transposing read land on disjoint banks.
+  constexpr int LDK = HD + 8;
+  constexpr int LDV = HD + 32;
+  constexpr int NM = HD / 16;          // MFMA steps over the head dim
+  constexpr int NDB = HD / 32;         // 32-wide output dim blocks
+  constexpr int CPR = HD / 8;          // 16-byte chunks per K/V row
+  constexpr int NCH = BN * CPR / 256;  // chunks per thread per tile (K and V each)
 
-  __shared__ __align__(16) uint16_t ks[BN * LDK];
-  __shared__ __align__(16) uint16_t vt[HD * LDV];
+  __shared__ __align__(16) uint16_t ks[2][BN * LDK];
+  __shared__ __align__(16) uint16_t vs[2][BN * LDV];
 
   const long n_qt = (a.n_q + kAttnBM - 1) / kAttnBM;
   const long tile = xcd_remap(blockIdx.x, n_qt * a.heads);
@@ -90,41 +93,25 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
 
   const uint16_t* kbase = a.k + head * HD;
   const uint16_t* vbase = a.v + head * HD;
-  const int vkg = tid / CPR;  // V key group (KPT keys)
-  const int vdg = tid % CPR;  // V dim group (8 dims)
 
-  u32x4 kreg[KCH], vreg[KPT];
+  u32x4 kreg[NCH], vreg[NCH];
   auto load = [&](long kv0) {
 #pragma unroll
-    for (int j = 0; j < KCH; ++j) {
+    for (int j = 0; j < NCH; ++j) {
       const int id = tid + 256 * j;
       const long key = kv0 + id / CPR;
-      kreg[j] = key < a.n_kv
-                    ? *reinterpret_cast<const u32x4*>(kbase + key * D + (id % CPR) * 8)
-                    : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const long key = kv0 + vkg * KPT + j;
-      vreg[j] = key < a.n_kv ? *reinterpret_cast<const u32x4*>(vbase + key * D + vdg * 8)
-                             : u32x4{0u, 0u, 0u, 0u};
+      const long off = key * D + (id % CPR) * 8;
+      const bool ok = key < a.n_kv;
+      kreg[j] = ok ? *reinterpret_cast<const u32x4*>(kbase + off) : u32x4{0u, 0u, 0u, 0u};
+      vreg[j] = ok ? *reinterpret_cast<const u32x4*>(vbase + off) : u32x4{0u, 0u, 0u, 0u};
     }
   };
-  auto store = [&]() {
+  auto store = [&](int buf) {
 #pragma unroll
-    for (int j = 0; j < KCH; ++j) {
+    for (int j = 0; j < NCH; ++j) {
       const int id = tid + 256 * j;
-      *reinterpret_cast<u32x4*>(&ks[(id / CPR) * LDK + (id % CPR) * 8]) = kreg[j];
-    }
-    const int pos = vt_pos(vkg * KPT);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      uint16_t* dst = &vt[(vdg * 8 + e) * LDV + pos];
-      if (KPT == 4) {
-        *reinterpret_cast<u32x2*>(dst) = u32x2{pair16(vreg[0], vreg[1], e), pair16(vreg[2], vreg[3], e)};
-      } else {
-        *reinterpret_cast<uint32_t*>(dst) = pair16(vreg[0], vreg[1], e);
-      }
+      *reinterpret_cast<u32x4*>(&ks[buf][(id / CPR) * LDK + (id % CPR) * 8]) = kreg[j];
+      *reinterpret_cast<u32x4*>(&vs[buf][(id / CPR) * LDV + (id % CPR) * 8]) = vreg[j];
     }
   };
 
@@ -137,27 +124,38 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   float l_run = 0.f;
   const float c = a.scale_log2;
 
+  // Per-lane offsets of the transposing V reads: group g = lane/16 covers
+  // keys 4*(g/2) + 0..3 (+8 for the second read) and dims 16*(g%2) + 0..15.
+  const int grp = lane >> 4, gl = lane & 15;
+  const int v_off = (4 * (grp >> 1) + (gl >> 2)) * LDV + 16 * (grp & 1) + 4 * (gl & 3);
+
   load(0);
-  store();
+  store(0);
+  if (BN < a.n_kv) load(BN);
   __syncthreads();
 
-  for (long kv0 = 0; kv0 < a.n_kv; kv0 += BN) {
-    const bool more = kv0 + BN < a.n_kv;
-    if (more) load(kv0 + BN);
+  const long n_tiles = (a.n_kv + BN - 1) / BN;
+  for (long t = 0; t < n_tiles; ++t) {
+    const int buf = static_cast<int>(t & 1);
+    const long kv0 = t * BN;
+    const uint16_t* kt = ks[buf];
+    const uint16_t* vt = vs[buf];
 
     // S^T block kb: keys 32*kb + 8*(r/4) + 4*hi + r%4 (r = 0..15), query l32.
     f32x16 s[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
 #pragma unroll
-      for (int m = 0; m < NM; ++m) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&ks[(kb * 32 + l32) * LDK + 16 * m + 8 * hi]);
+    for (int m = 0; m < NM; ++m) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&kt[(kb * 32 + l32) * LDK + 16 * m + 8 * hi]);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[m], s[kb], 0, 0, 0);
       }
     }
-    if (!more && kv0 + BN > a.n_kv) {
+    if (kv0 + BN > a.n_kv) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -176,7 +174,8 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
     const float m_new = fmaxf(m_run, mx * c);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
 
-    // Probabilities, packed as the B operand of the four 16-key PV chunks.
+    // Probabilities, packed as the B operand of the four 16-key PV chunks:
+    // chunk ch = 2*kb + r/8, slot 8*hi + 4*((r/4)%2) + r%4 <-> key 16*ch + 8*((r/4)%2) + 4*hi + r%4.
     bf16x8 pf[4];
     float psum = 0.f;
 #pragma unroll
@@ -196,21 +195,26 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
     }
     m_run = m_new;
 
-    // O^T[dim, query] += V^T[dim, key] P^T[key, query], 16 keys per MFMA.
+    // O^T[dim, query] += V^T[dim, key] P^T[key, query], 16 keys per MFMA; the
+    // A operand (V^T) comes from two transposing reads of row-major V.
 #pragma unroll
     for (int ch = 0; ch < 4; ++ch) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&vt[(db * 32 + l32) * LDV + 16 * ch + 8 * hi]);
+        const uint16_t* vp = vt + 16 * ch * LDV + 32 * db + v_off;
+        const v4i16 lo = ds_read_tr16(vp);
+        const v4i16 hi4 = ds_read_tr16(vp + 8 * LDV);
+        const bf16x8 vf = __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ch], acc[db], 0, 0, 0);
       }
     }
 
+    // Stage tile t+1 (already in registers) into the other buffer, then fetch t+2.
+    // The other buffer was last read during tile t-1, before the previous barrier.
+    if (t + 1 < n_tiles) store(buf ^ 1);
     __syncthreads();
-    if (more) {
-      store();
-      __syncthreads();
-    }
+    if (t + 2 < n_tiles) load(kv0 + 2 * BN);
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
