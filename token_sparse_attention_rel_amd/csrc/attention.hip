@@ -20,13 +20,15 @@
 // are exactly the B operand it must supply, provided the V^T operand uses
 // the same key order inside each 16-key chunk -- which the transposing LDS
 // reads of row-major V deliver directly.  No probabilities travel through LDS.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace tsa {
 
 constexpr int kAttnBM = 128;  // queries per workgroup
-constexpr int kAttnBN = 64;   // keys per tile
+constexpr int kAttnBN = 32;   // keys per tile
 
 struct AttnArgs {
   const uint16_t* q;
@@ -54,6 +56,22 @@ __device__ __forceinline__ v4i16 ds_read_tr16(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)const_cast<uint16_t*>(p));
 }
 
+// Softmax rescale policy: the running max used for the exponent, m, is only
+// moved when a new score exceeds it by more than kLazyMax (log2 units), so
+// probabilities stay <= 2**kLazyMax and the O rescale is almost never needed.
+// Any consistent shift gives the same normalised output.
+constexpr float kLazyMax = 8.0f;
+
+// MFMA / VALU / LDS instruction classes for the scheduler hints.
+constexpr int kSchedMfma = 0x008, kSchedValu = 0x002, kSchedDsRead = 0x100;
+
+// Word 3 of a raw buffer resource on gfx9-class GPUs (32-bit elements, no swizzle);
+// out-of-range offsets then read as zero.
+constexpr int kBufferRsrcFlags = 0x00020000;
+
+template <bool B>
+using Flag = std::integral_constant<bool, B>;
+
 template <int HD>
 __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   constexpr int BN = kAttnBN;
@@ -66,6 +84,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   constexpr int NDB = HD / 32;         // 32-wide output dim blocks
   constexpr int CPR = HD / 8;          // 16-byte chunks per K/V row
   constexpr int NCH = BN * CPR / 256;  // chunks per thread per tile (K and V each)
+  static_assert(NCH >= 1, "tile too small for the workgroup");
 
   __shared__ __align__(16) uint16_t ks[2][BN * LDK];
   __shared__ __align__(16) uint16_t vs[2][BN * LDV];
@@ -91,114 +110,65 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
     }
   }
 
-  const uint16_t* kbase = a.k + head * HD;
-  const uint16_t* vbase = a.v + head * HD;
-
-  u32x4 kreg[NCH], vreg[NCH];
-  auto load = [&](long kv0) {
+  // K/V tiles are fetched with range-checked buffer loads: rows past the end
+  // of the cache read as zeros, so prefetches beyond the last tile need no branch.
+  const long n_kv = a.n_kv;
+  const int kv_bytes = static_cast<int>(((n_kv - 1) * D + HD) * 2);
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.k + head * HD), 0, kv_bytes, kBufferRsrcFlags);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.v + head * HD), 0, kv_bytes, kBufferRsrcFlags);
+  // Loader: chunk id = tid + 256*j covers row id / CPR, 16-byte column id % CPR.
+  int g_off[NCH];
+  uint32_t k_lds[NCH], v_lds[NCH];
 #pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const int id = tid + 256 * j;
-      const long key = kv0 + id / CPR;
-      const long off = key * D + (id % CPR) * 8;
-      const bool ok = key < a.n_kv;
-      kreg[j] = ok ? *reinterpret_cast<const u32x4*>(kbase + off) : u32x4{0u, 0u, 0u, 0u};
-      vreg[j] = ok ? *reinterpret_cast<const u32x4*>(vbase + off) : u32x4{0u, 0u, 0u, 0u};
+  for (int j = 0; j < NCH; ++j) {
+    const int id = tid + 256 * j;
+    g_off[j] = static_cast<int>(((id / CPR) * D + (id % CPR) * 8) * 2);
+    k_lds[j] = (id / CPR) * LDK + (id % CPR) * 8;
+    v_lds[j] = (id / CPR) * LDV + (id % CPR) * 8;
+  }
+  auto gload = [&](u32x4* r, __amdgpu_buffer_rsrc_t rs, long kv0) {
+    const long boff = kv0 * D * 2;
+    const int so = boff < kv_bytes ? static_cast<int>(boff) : kv_bytes;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j)
+      r[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, g_off[j], so, 0));
+  };
+  auto sstore = [&](uint16_t* buf, const uint32_t* off, const u32x4* r) {
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) *reinterpret_cast<u32x4*>(buf + off[j]) = r[j];
+  };
+
+  // S^T block (32 keys x 32 queries): keys 8*(r/4) + 4*hi + r%4 (r = 0..15), query l32.
+  auto qk = [&](const uint16_t* kt) {
+    f32x16 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+        *reinterpret_cast<const bf16x8*>(&kt[l32 * LDK + 8 * hi]), qf[0], f32x16{}, 0, 0, 0);
+#pragma unroll
+    for (int m = 1; m < NM; ++m)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          *reinterpret_cast<const bf16x8*>(&kt[l32 * LDK + 16 * m + 8 * hi]), qf[m], s, 0, 0, 0);
+    return s;
+  };
+  auto mask_tail = [&](f32x16& s, long kv0) {
+    if (kv0 + BN > n_kv) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (kv0 + 8 * (r >> 2) + 4 * hi + (r & 3) >= n_kv) s[r] = -__builtin_inff();
     }
   };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const int id = tid + 256 * j;
-      *reinterpret_cast<u32x4*>(&ks[buf][(id / CPR) * LDK + (id % CPR) * 8]) = kreg[j];
-      *reinterpret_cast<u32x4*>(&vs[buf][(id / CPR) * LDV + (id % CPR) * 8]) = vreg[j];
-    }
-  };
 
-  f32x16 acc[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
-  float m_run = -__builtin_inff();
-  float l_run = 0.f;
-  const float c = a.scale_log2;
-
-  // Per-lane offsets of the transposing V reads: group g = lane/16 covers
-  // keys 4*(g/2) + 0..3 (+8 for the second read) and dims 16*(g%2) + 0..15.
+  // Transposing V reads: group g = lane/16 covers keys 4*(g/2) + 0..3 (+8 for the
+  // second read) and dims 16*(g%2) + 0..15 of each 32-wide dim block.
   const int grp = lane >> 4, gl = lane & 15;
   const int v_off = (4 * (grp >> 1) + (gl >> 2)) * LDV + 16 * (grp & 1) + 4 * (gl & 3);
-
-  load(0);
-  store(0);
-  if (BN < a.n_kv) load(BN);
-  __syncthreads();
-
-  const long n_tiles = (a.n_kv + BN - 1) / BN;
-  for (long t = 0; t < n_tiles; ++t) {
-    const int buf = static_cast<int>(t & 1);
-    const long kv0 = t * BN;
-    const uint16_t* kt = ks[buf];
-    const uint16_t* vt = vs[buf];
-
-    // S^T block kb: keys 32*kb + 8*(r/4) + 4*hi + r%4 (r = 0..15), query l32.
-    f32x16 s[2];
+  f32x16 acc[NDB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+  // O^T[dim, query] += V^T[dim, key] P^T[key, query] over one 32-key tile (two 16-key chunks).
+  auto pv = [&](const uint16_t* vt, const bf16x8* pf) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&kt[(kb * 32 + l32) * LDK + 16 * m + 8 * hi]);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[m], s[kb], 0, 0, 0);
-      }
-    }
-    if (kv0 + BN > a.n_kv) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const long key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (key >= a.n_kv) s[kb][r] = -__builtin_inff();
-        }
-    }
-
-    float mx = -__builtin_inff();
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx * c);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-
-    // Probabilities, packed as the B operand of the four 16-key PV chunks:
-    // chunk ch = 2*kb + r/8, slot 8*hi + 4*((r/4)%2) + r%4 <-> key 16*ch + 8*((r/4)%2) + 4*hi + r%4.
-    bf16x8 pf[4];
-    float psum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -m_new));
-        psum += p;
-        pf[2 * kb + (r >> 3)][r & 7] = static_cast<__bf16>(p);
-      }
-    l_run = fmaf(l_run, alpha, psum);
-    if (__ballot(alpha != 1.f)) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-    }
-    m_run = m_new;
-
-    // O^T[dim, query] += V^T[dim, key] P^T[key, query], 16 keys per MFMA; the
-    // A operand (V^T) comes from two transposing reads of row-major V.
-#pragma unroll
-    for (int ch = 0; ch < 4; ++ch) {
+    for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const uint16_t* vp = vt + 16 * ch * LDV + 32 * db + v_off;
@@ -208,14 +178,101 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
             bf16x8, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ch], acc[db], 0, 0, 0);
       }
-    }
+  };
 
-    // Stage tile t+1 (already in registers) into the other buffer, then fetch t+2.
-    // The other buffer was last read during tile t-1, before the previous barrier.
-    if (t + 1 < n_tiles) store(buf ^ 1);
+  float m_run = -__builtin_inff();
+  float l_run = 0.f;
+  const float c = a.scale_log2;
+  const long n_t = (n_kv + BN - 1) / BN;
+
+  // Prologue: K tiles 0 and 1 in LDS, S of tile 0; registers hold K(2) and V(0).
+  u32x4 kr[NCH], vr[NCH];
+  gload(kr, krs, 0);
+  sstore(ks[0], k_lds, kr);
+  gload(kr, krs, BN);
+  sstore(ks[1], k_lds, kr);
+  __syncthreads();
+  gload(kr, krs, 2 * BN);
+  gload(vr, vrs, 0);
+  f32x16 s_cur = qk(ks[0]);
+  mask_tail(s_cur, 0);
+  __syncthreads();  // every wave is done with K(0) before K(2) overwrites it
+
+  bf16x8 p_prev[2];
+  // Iteration t: MFMA work PV(t-1) and QK(t+1) interleaved with the softmax of
+  // tile t on the VALU; then stage V(t) and K(t+2) and fetch V(t+1) and K(t+3).
+  // A buffer is rewritten only after the barrier that follows its last read.
+  auto iteration = [&](long t, auto has_prev, auto has_next, auto may_mask) {
+    const int b = static_cast<int>(t & 1);
+    f32x16 s_next;
+    if constexpr (decltype(has_prev)::value) pv(vs[b ^ 1], p_prev);
+    if constexpr (decltype(has_next)::value) s_next = qk(ks[b ^ 1]);
+
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float cand = mx * c;
+    const bool upd = cand > m_run + kLazyMax;
+    const float m_new = upd ? cand : m_run;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    bf16x8 pf[2];
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(s_cur[r], c, -m_new));
+      psum += p;
+      pf[r >> 3][r & 7] = static_cast<__bf16>(p);
+    }
+    l_run = fmaf(l_run, alpha, psum);
+    {
+      // Keep the softmax in this block: its results are consumed only in the next
+      // iteration, and left alone the compiler sinks it past the barrier, where it
+      // can no longer overlap the MFMAs above.  (An empty asm that reads them.)
+      const u32x4 p0 = __builtin_bit_cast(u32x4, pf[0]), p1 = __builtin_bit_cast(u32x4, pf[1]);
+      asm volatile("" ::"v"(p0[0]), "v"(p0[1]), "v"(p0[2]), "v"(p0[3]), "v"(p1[0]), "v"(p1[1]),
+                   "v"(p1[2]), "v"(p1[3]), "v"(l_run), "v"(alpha));
+    }
+    if constexpr (decltype(has_prev)::value && decltype(has_next)::value) {
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * NDB + NM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedValu, 5, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (decltype(may_mask)::value) mask_tail(s_next, (t + 1) * BN);
+
+    sstore(vs[b], v_lds, vr);
+    sstore(ks[b], k_lds, kr);
     __syncthreads();
-    if (t + 2 < n_tiles) load(kv0 + 2 * BN);
+    gload(vr, vrs, (t + 1) * BN);
+    gload(kr, krs, (t + 3) * BN);
+    if constexpr (decltype(has_next)::value) s_cur = s_next;
+    p_prev[0] = pf[0];
+    p_prev[1] = pf[1];
+    // O now holds tiles < t (PV(t-1) was issued above) at the old max: bring it
+    // to the new one before PV(t) is added in the next iteration.
+    if (__ballot(upd)) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+    }
+  };
+
+  if (n_t == 1) {
+    iteration(0, Flag<false>{}, Flag<false>{}, Flag<false>{});
+  } else {
+    iteration(0, Flag<false>{}, Flag<true>{}, Flag<true>{});
+    for (long t = 1; t + 2 < n_t; ++t) iteration(t, Flag<true>{}, Flag<true>{}, Flag<false>{});
+    if (n_t > 2) iteration(n_t - 2, Flag<true>{}, Flag<true>{}, Flag<true>{});
+    iteration(n_t - 1, Flag<true>{}, Flag<false>{}, Flag<false>{});
   }
+  pv(vs[(n_t - 1) & 1], p_prev);
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (qvalid) {
