@@ -1,0 +1,116 @@
+"""Write the text summaries under profiles/ from rocprofv3 CSV output.
+
+Usage (repository root, after the GPU runs listed in each summary wrote gpurun_out/):
+    python profiles/make_summaries.py gpurun_out
+Reads <dir>/prof_trace/run_kernel_trace.csv + run_kernel_stats.csv + prof_trace.log (the
+bench JSON line printed under the profiler), and <dir>/pmc_{fetch,write,copy_fetch,copy_write}.
+"""
+
+from __future__ import annotations
+
+import collections
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ATTN = "attention_kernel<128>"
+FLOP = 4 * 9828 * 32760 * 128 * 12
+ALGO_BYTES = 9828 * 1536 * 2 + 2 * 32760 * 1536 * 2 + 9828 * 1536 * 2
+
+
+def _short(name):
+    return name.split("(")[0].replace("void ", "")
+
+
+def trace_summary(d):
+    stats = list(csv.DictReader(open(os.path.join(d, "prof_trace", "run_kernel_stats.csv"))))
+    trace = list(csv.DictReader(open(os.path.join(d, "prof_trace", "run_kernel_trace.csv"))))
+    bench = None
+    log = os.path.join(d, "prof_trace.log")
+    if os.path.exists(log):
+        for line in open(log):
+            if line.startswith("{"):
+                bench = json.loads(line)
+    warm = int(bench["warmup"]) if bench else 3
+    durs = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in trace if ATTN in r["Kernel_Name"]]
+    timed = durs[warm:] if len(durs) > warm else durs
+    out = [
+        "# rocprofv3 kernel-trace summary: pruned layer step, wan13b workload",
+        "# (N=32760 tokens, D=1536, 12 heads x 128, 30% active = 9828 queries)",
+        "# command (repository root, one MI355X):",
+        "#   rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_trace -o run -- \\",
+        "#       python3 bench.py --steps 10 --warmup 3 --no-cpu-baseline --no-dense",
+        "# summary written by: python profiles/make_summaries.py gpurun_out",
+        "",
+        f"{'kernel':48s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>6s}",
+    ]
+    for r in stats:
+        out.append(f"{_short(r['Name'])[:48]:48s} {r['Calls']:>6s} {float(r['AverageNs'])/1e3:10.1f} "
+                   f"{float(r['MinNs'])/1e3:10.1f} {float(r['MaxNs'])/1e3:10.1f} {float(r['Percentage']):6.2f}")
+    avg_t = sum(timed) / len(timed) / 1e3
+    out += ["", f"# {ATTN}: {len(durs)} dispatches; the {len(timed)} of the timed steps average {avg_t:.1f} us",
+            f"#   -> {FLOP / (avg_t * 1e-6) / 1e12:.1f} TFLOP/s = {FLOP / (avg_t * 1e-6) / 1e12 / 2500 * 100:.1f}% of 2500 TFLOP/s"]
+    if bench:
+        out.append(f"# bench.py under the profiler (HIP events on the launch stream): attention "
+                   f"{bench['kernel_ms']['attention_scatter']*1e3:.1f} us, roofline.achieved {bench['roofline']['achieved']} TFLOP/s")
+    return "\n".join(out) + "\n"
+
+
+def _per_kernel(d, counter):
+    f = glob.glob(os.path.join(d, "*counter_collection.csv"))[0]
+    agg = collections.defaultdict(list)
+    for r in csv.DictReader(open(f)):
+        if r["Counter_Name"] == counter:
+            agg[_short(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in agg.items()}
+
+
+def traffic_summary(d):
+    fetch = _per_kernel(os.path.join(d, "pmc_fetch"), "FETCH_SIZE")
+    write = _per_kernel(os.path.join(d, "pmc_write"), "WRITE_SIZE")
+    cf = _per_kernel(os.path.join(d, "pmc_copy_fetch"), "FETCH_SIZE")["__amd_rocclr_copyBuffer"]
+    cw = _per_kernel(os.path.join(d, "pmc_copy_write"), "WRITE_SIZE")["__amd_rocclr_copyBuffer"]
+    sf, sw = 2 ** 20 / cf, 2 ** 20 / cw
+    src = hashlib.sha256(open(os.path.join(ROOT, "token_sparse_attention_rel_amd", "csrc", "attention.hip"), "rb").read()).hexdigest()
+    a = next(k for k in fetch if ATTN in k)
+    hb = fetch[a] * sf * 1024 + write[a] * sw * 1024
+    out = [
+        "# HBM traffic per launch from rocprofv3 counters, wan13b pruned layer step",
+        "# commands (repository root, one MI355X; one counter per run):",
+        "#   timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-dense",
+        "#   timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-dense",
+        "# calibration: the same two counters over `python3 bench.py --copy-calibration` (a plain 1 GiB",
+        "#   device copy, __amd_rocclr_copyBuffer, reading and writing exactly 1048576 KiB per launch):",
+        f"#   FETCH_SIZE reads {cf:.1f} KiB per copy -> scale {sf:.4f};  WRITE_SIZE reads {cw:.1f} KiB -> scale {sw:.4f}",
+        "# summary written by: python profiles/make_summaries.py gpurun_out",
+        "# per-kernel averages over dispatches (KiB as reported, then scaled bytes):",
+        "",
+    ]
+    for k in fetch:
+        if k.startswith("at::"):
+            continue
+        fb, wb = fetch[k] * sf * 1024, write.get(k, 0) * sw * 1024
+        out.append(f"# {k[:40]:40s} FETCH {fetch[k]:12.1f} KiB  WRITE {write.get(k, 0):12.1f} KiB  -> read {fb/1e6:9.1f} MB  write {wb/1e6:8.1f} MB")
+    out += ["", "# attention kernel: algorithmic bytes per launch = Q_a + K + V + O",
+            f"#   = 9828*1536*2 + 2*32760*1536*2 + 9828*1536*2 = {ALGO_BYTES/1e6:.1f} MB;"
+            f" measured/algorithmic = {hb / ALGO_BYTES:.2f}",
+            f"kernel: {ATTN}", f"kernel_source_sha256: {src}",
+            f"fetch_kib_per_dispatch: {fetch[a]:.3f}", f"write_kib_per_dispatch: {write[a]:.3f}",
+            f"fetch_scale: {sf:.5f}", f"write_scale: {sw:.5f}", f"hbm_bytes_per_launch: {hb:.0f}"]
+    return "\n".join(out) + "\n"
+
+
+def main(argv):
+    d = argv[1] if len(argv) > 1 else "gpurun_out"
+    here = os.path.dirname(os.path.abspath(__file__))
+    open(os.path.join(here, "layer_step_wan13b_kernel_trace.txt"), "w").write(trace_summary(d))
+    open(os.path.join(here, "attention_wan13b_traffic.txt"), "w").write(traffic_summary(d))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv))

@@ -6,7 +6,8 @@
 // bidirectional softmax attention, no mask.
 //
 // Flash-style single pass with an online softmax, bf16 MFMA, fp32 state.
-// A workgroup of 4 waves owns 128 queries of one head; each wave owns 32.
+// A workgroup of 8 waves (4 for head_dim 64) owns 32 queries per wave of one
+// head.
 // Key/value tiles of 64 rows are staged row-major through two LDS buffers
 // (one barrier per tile); the next tile's global loads are in flight while
 // the current one is computed.
@@ -27,8 +28,13 @@
 
 namespace tsa {
 
-constexpr int kAttnBM = 128;  // queries per workgroup
-constexpr int kAttnBN = 32;   // keys per tile
+constexpr int kAttnBN = 32;  // keys per tile
+
+// Waves per workgroup (32 queries each): 8 for head_dim 128, so every thread
+// stages one 16-byte chunk of K and of V per tile and one K/V tile in LDS feeds
+// 256 queries; 4 for head_dim 64 (a 32 x 64 tile has 256 chunks).
+template <int HD>
+constexpr int attn_waves() { return HD == 128 ? 8 : 4; }
 
 struct AttnArgs {
   const uint16_t* q;
@@ -62,9 +68,6 @@ __device__ __forceinline__ v4i16 ds_read_tr16(const uint16_t* p) {
 // Any consistent shift gives the same normalised output.
 constexpr float kLazyMax = 8.0f;
 
-// MFMA / VALU / LDS instruction classes for the scheduler hints.
-constexpr int kSchedMfma = 0x008, kSchedValu = 0x002, kSchedDsRead = 0x100;
-
 // Word 3 of a raw buffer resource on gfx9-class GPUs (32-bit elements, no swizzle);
 // out-of-range offsets then read as zero.
 constexpr int kBufferRsrcFlags = 0x00020000;
@@ -73,8 +76,10 @@ template <bool B>
 using Flag = std::integral_constant<bool, B>;
 
 template <int HD>
-__global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * attn_waves<HD>(), 2) void attention_kernel(AttnArgs a) {
   constexpr int BN = kAttnBN;
+  constexpr int NT = 64 * attn_waves<HD>();  // threads
+  constexpr int BM = 32 * attn_waves<HD>();  // queries per workgroup
   // K rows: stride HD+8 elements (16-byte reads down a column hit distinct banks).
   // V rows: stride HD+32 elements = 64 mod 256 bytes, so the four rows touched by
   // a 32-lane half of a transposing read land on disjoint banks.
@@ -83,14 +88,14 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   constexpr int NM = HD / 16;          // MFMA steps over the head dim
   constexpr int NDB = HD / 32;         // 32-wide output dim blocks
   constexpr int CPR = HD / 8;          // 16-byte chunks per K/V row
-  constexpr int NCH = BN * CPR / 256;  // chunks per thread per tile (K and V each)
+  constexpr int NCH = BN * CPR / NT;   // chunks per thread per tile (K and V each)
   static_assert(NCH >= 1, "tile too small for the workgroup");
 
   __shared__ __align__(16) uint16_t ks[2][BN * LDK];
   __shared__ __align__(16) uint16_t vs[2][BN * LDV];
 
-  const long n_qt = (a.n_q + kAttnBM - 1) / kAttnBM;
-  const long tile = xcd_remap(blockIdx.x, n_qt * a.heads);
+  const long n_qt = (a.n_q + BM - 1) / BM;
+  const long tile = blockIdx.x;
   const int head = static_cast<int>(tile / n_qt);
   const long qt = tile - static_cast<long>(head) * n_qt;
 
@@ -98,7 +103,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
 
-  const long qrow = qt * kAttnBM + wave * 32 + l32;
+  const long qrow = qt * BM + wave * 32 + l32;
   const bool qvalid = qrow < a.n_q;
   bf16x8 qf[NM];
   {
@@ -118,12 +123,12 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
       const_cast<uint16_t*>(a.k + head * HD), 0, kv_bytes, kBufferRsrcFlags);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(a.v + head * HD), 0, kv_bytes, kBufferRsrcFlags);
-  // Loader: chunk id = tid + 256*j covers row id / CPR, 16-byte column id % CPR.
+  // Loader: chunk id = tid + NT*j covers row id / CPR, 16-byte column id % CPR.
   int g_off[NCH];
   uint32_t k_lds[NCH], v_lds[NCH];
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
-    const int id = tid + 256 * j;
+    const int id = tid + NT * j;
     g_off[j] = static_cast<int>(((id / CPR) * D + (id % CPR) * 8) * 2);
     k_lds[j] = (id / CPR) * LDK + (id % CPR) * 8;
     v_lds[j] = (id / CPR) * LDV + (id % CPR) * 8;
@@ -234,15 +239,6 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
       asm volatile("" ::"v"(p0[0]), "v"(p0[1]), "v"(p0[2]), "v"(p0[3]), "v"(p1[0]), "v"(p1[1]),
                    "v"(p1[2]), "v"(p1[3]), "v"(l_run), "v"(alpha));
     }
-    if constexpr (decltype(has_prev)::value && decltype(has_next)::value) {
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 0);
-#pragma unroll
-      for (int i = 0; i < 2 * NDB + NM; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedValu, 5, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-      }
-    }
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (decltype(may_mask)::value) mask_tail(s_next, (t + 1) * BN);
 
@@ -305,12 +301,14 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t
   a.out = out;
   a.out_rows = out_rows;
   a.lse = lse;
-  const long n_qt = (n_q + kAttnBM - 1) / kAttnBM;
-  const dim3 grid(static_cast<unsigned>(n_qt * heads));
   if (head_dim == 128) {
-    hipLaunchKernelGGL(attention_kernel<128>, grid, dim3(256), 0, s, a);
+    constexpr int bm = 32 * attn_waves<128>();
+    const dim3 grid(static_cast<unsigned>((n_q + bm - 1) / bm * heads));
+    hipLaunchKernelGGL(attention_kernel<128>, grid, dim3(64 * attn_waves<128>()), 0, s, a);
   } else {
-    hipLaunchKernelGGL(attention_kernel<64>, grid, dim3(256), 0, s, a);
+    constexpr int bm = 32 * attn_waves<64>();
+    const dim3 grid(static_cast<unsigned>((n_q + bm - 1) / bm * heads));
+    hipLaunchKernelGGL(attention_kernel<64>, grid, dim3(64 * attn_waves<64>()), 0, s, a);
   }
   return hipGetLastError();
 }
