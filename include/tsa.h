@@ -155,7 +155,8 @@ tsa_status tsa_assign_groups(const float* scores, int64_t n, int n_groups,
  *                to row rows[r] (rows required, each < n_cache) -- this fuses
  *                the cache sync (a6) into the projection.
  *   eps          device bf16 [n_x_rows, dim] or NULL (no recovery).
- * dim must be a multiple of 64.
+ * dim must be a multiple of 64; n_x_rows*dim*2 and 3*dim*dim*2 must each be below
+ * 2^31 bytes (32-bit buffer ranges).
  * Errors: INVALID_ARG, SHAPE, DTYPE, ALIGNMENT, HIP.
  */
 tsa_status tsa_qkv_active(const void* x, int x_dtype, int64_t n_x_rows, const int32_t* rows,
@@ -192,6 +193,7 @@ tsa_status tsa_kv_cache_sync(const tsa_bf16* k_a, const tsa_bf16* v_a, const int
  *            otherwise [n_out, dim] with row r written to row out_rows[r]
  *            (this fuses the scatter, a8); other rows are not touched.
  *   lse_out  device f32 [heads, n_q] natural-log normaliser log sum_j exp(scale*s_j), or NULL.
+ * n_kv*heads*head_dim*2 must be below 2^31 bytes (32-bit buffer range of the cache).
  * Errors: INVALID_ARG, SHAPE, ALIGNMENT, HIP.
  */
 tsa_status tsa_sparse_query_attention(const tsa_bf16* q, const tsa_bf16* k_cache,

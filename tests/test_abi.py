@@ -103,6 +103,9 @@ def test_qkv_validation():
     assert qkv(w=U) == B.ERR_ALIGNMENT
     assert qkv(eps=A, sigma=float("nan")) == B.ERR_INVALID_ARG
     assert qkv(rows=A + 2) == B.ERR_ALIGNMENT
+    # 32-bit buffer ranges: 2^20 rows of 1024 bf16 = 2 GiB is one byte too many
+    assert qkv(nx=1 << 20, dim=1024) == B.ERR_SHAPE
+    assert qkv(dim=19008) == B.ERR_SHAPE  # 3*D*D*2 >= 2^31
 
 
 def attn(**kw):
@@ -124,6 +127,7 @@ def test_attention_validation():
     assert attn(scale=float("inf")) == B.ERR_INVALID_ARG
     assert attn(k=U) == B.ERR_ALIGNMENT
     assert attn(lse=A + 2) == B.ERR_ALIGNMENT
+    assert attn(nkv=1 << 20, heads=8, hd=128) == B.ERR_SHAPE  # cache of 2 GiB
 
 
 def test_row_mover_validation():

@@ -93,7 +93,7 @@ def _exact_score_rows(values, dim=64, seed=0):
     return x_cur, x_ref
 
 
-@pytest.mark.parametrize("n", [1, 7, 100, 4096, 4099, 20000])
+@pytest.mark.parametrize("n", [1, 7, 100, 4096, 4099, 12000, 20000, 32768, 40000])
 def test_topk_select_and_compact_bit_exact_with_ties(n):
     t = tsa()
     r = np.random.default_rng(n)

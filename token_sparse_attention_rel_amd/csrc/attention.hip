@@ -95,7 +95,7 @@ __global__ __launch_bounds__(64 * attn_waves<HD>(), 2) void attention_kernel(Att
   __shared__ __align__(16) uint16_t vs[2][BN * LDV];
 
   const long n_qt = (a.n_q + BM - 1) / BM;
-  const long tile = blockIdx.x;
+  const long tile = xcd_remap(blockIdx.x, n_qt * a.heads);
   const int head = static_cast<int>(tile / n_qt);
   const long qt = tile - static_cast<long>(head) * n_qt;
 

@@ -15,8 +15,10 @@
 // the cache sync is fused.
 //
 // Tile: 128 output features x 128 tokens x 64 (K) per step, 4 waves in a 2x2
-// arrangement, each wave 64 x 64 (2 x 2 MFMA blocks).  Global -> register
-// prefetch of the next K step overlaps the MFMAs of the current one.
+// arrangement, each wave 64 x 64 (2 x 2 MFMA blocks).  Two LDS buffers (one
+// barrier per K step); the registers prefetch the K step after next while the
+// current one is multiplied.  bf16 rows arrive through range-checked buffer
+// loads (invalid rows read as zeros, no per-step selects).
 #include "common.h"
 #include "kernels.h"
 
@@ -47,13 +49,20 @@ struct GemmArgs {
   int to_cache;
 };
 
+// Word 3 of a raw buffer resource on gfx9-class GPUs; offsets past num_records read zero.
+constexpr int kBufferRsrcFlags = 0x00020000;
+// A per-lane offset that is always out of range: the load returns zeros.
+constexpr int kOutOfRange = 0x7FFFFFF0;
+
+// Token tiles handled together per XCD: the workgroups that run at the same
+// time on one XCD then share few W panels and few token tiles in its L2.
+constexpr int kTokGroup = 8;
+
 template <int SRC>
-__device__ __forceinline__ u32x4 load_a_chunk(const GemmArgs& a, long tok, bool valid,
-                                              bool has_clean, long k0) {
+__device__ __forceinline__ u32x4 load_a_chunk_slow(const GemmArgs& a, long tok, bool valid,
+                                                   bool has_clean, long k0) {
   if (!valid) return u32x4{0u, 0u, 0u, 0u};
-  if (SRC == kSrcBf16) {
-    return *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.x) + tok * a.dim + k0);
-  } else if (SRC == kSrcF32) {
+  if (SRC == kSrcF32) {
     const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(a.x) + tok * a.dim + k0);
     const f32x4 lo = p[0], hi = p[1];
     return u32x4{pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]), pack_bf16x2(hi[0], hi[1]),
@@ -78,46 +87,66 @@ __device__ __forceinline__ u32x4 load_a_chunk(const GemmArgs& a, long tok, bool 
 
 template <int SRC>
 __global__ __launch_bounds__(256, 2) void qkv_gemm_kernel(GemmArgs a) {
-  __shared__ __align__(16) uint16_t ws[kGemmBM * kGemmLD];
-  __shared__ __align__(16) uint16_t as[kGemmBN * kGemmLD];
+  __shared__ __align__(16) uint16_t ws[2][kGemmBM * kGemmLD];
+  __shared__ __align__(16) uint16_t as[2][kGemmBN * kGemmLD];
+
+  // Tile order: XCD-aware, then groups of kTokGroup token tiles with the token
+  // tile varying fastest, so concurrently running workgroups share W panels.
+  const long n_col = (a.ncols + kGemmBM - 1) / kGemmBM;
+  const long n_tok = (a.n + kGemmBN - 1) / kGemmBN;
+  const long L = xcd_remap(blockIdx.x, n_col * n_tok);
+  const long grp = L / (kTokGroup * n_col);
+  const long first_tok = grp * kTokGroup;
+  const long gsize = (n_tok - first_tok) < kTokGroup ? (n_tok - first_tok) : kTokGroup;
+  const long local = L - grp * kTokGroup * n_col;
+  const long tok_tile = first_tok + local % gsize;
+  const long col_tile = local / gsize;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const long c_base = a.col0 + static_cast<long>(blockIdx.x) * kGemmBM;  // absolute feature
-  const long t_base = static_cast<long>(blockIdx.y) * kGemmBN;            // compact token row
+  const long c_base = a.col0 + col_tile * kGemmBM;  // absolute feature
+  const long t_base = tok_tile * kGemmBN;            // compact token row
   const long c_end = a.col0 + a.ncols;
 
-  // Loader slots: 4 rows per thread of each tile, 16-byte chunk (tid & 7) of the K slice.
+  // Loader slots: rows lrow + 32*j of each tile, 16-byte chunk (tid & 7) of the K slice.
   const int lrow = tid >> 3;
   const int lcol = (tid & 7) * 8;
-  const uint16_t* wrow[4];
-  bool wvalid[4];
+  const long dim = a.dim;
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.w), 0, static_cast<int>(3 * dim * dim * 2), kBufferRsrcFlags);
+  const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(a.x), 0, static_cast<int>(a.n_x_rows * dim * 2), kBufferRsrcFlags);
+  int w_off[4], x_off[4];
   long tok[4];
   bool tvalid[4], tclean[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const long c = c_base + lrow + 32 * j;
-    wvalid[j] = c < c_end;
-    wrow[j] = a.w + (wvalid[j] ? c : 0) * a.dim + lcol;
+    w_off[j] = c < c_end ? static_cast<int>((c * dim + lcol) * 2) : kOutOfRange;
     const long r = t_base + lrow + 32 * j;
     tvalid[j] = r < a.n;
     tok[j] = tvalid[j] ? (a.rows ? static_cast<long>(a.rows[r]) : r) : 0;
+    x_off[j] = tvalid[j] ? static_cast<int>((tok[j] * dim + lcol) * 2) : kOutOfRange;
     const long src = tok[j] - a.src_off;
     tclean[j] = src >= 0 && src < a.n_x_rows;
   }
 
   u32x4 wreg[4], areg[4];
   auto load_tiles = [&](long k0) {
+    const int so = static_cast<int>(k0 * 2);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      wreg[j] = wvalid[j] ? *reinterpret_cast<const u32x4*>(wrow[j] + k0) : u32x4{0u, 0u, 0u, 0u};
-      areg[j] = load_a_chunk<SRC>(a, tok[j], tvalid[j], tclean[j], k0 + lcol);
+      wreg[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, w_off[j], so, 0));
+      if constexpr (SRC == kSrcBf16)
+        areg[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, x_off[j], so, 0));
+      else
+        areg[j] = load_a_chunk_slow<SRC>(a, tok[j], tvalid[j], tclean[j], k0 + lcol);
     }
   };
-  auto store_tiles = [&]() {
+  auto store_tiles = [&](int buf) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      *reinterpret_cast<u32x4*>(&ws[(lrow + 32 * j) * kGemmLD + lcol]) = wreg[j];
-      *reinterpret_cast<u32x4*>(&as[(lrow + 32 * j) * kGemmLD + lcol]) = areg[j];
+      *reinterpret_cast<u32x4*>(&ws[buf][(lrow + 32 * j) * kGemmLD + lcol]) = wreg[j];
+      *reinterpret_cast<u32x4*>(&as[buf][(lrow + 32 * j) * kGemmLD + lcol]) = areg[j];
     }
   };
 
@@ -127,40 +156,39 @@ __global__ __launch_bounds__(256, 2) void qkv_gemm_kernel(GemmArgs a) {
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
+  const long n_k = dim / kGemmBK;
   load_tiles(0);
-  store_tiles();
+  store_tiles(0);
+  if (n_k > 1) load_tiles(kGemmBK);
   __syncthreads();
 
   const int l32 = lane & 31;
   const int khalf = (lane >> 5) * 8;
-  for (long k0 = 0; k0 < a.dim; k0 += kGemmBK) {
-    const bool more = k0 + kGemmBK < a.dim;
-    if (more) load_tiles(k0 + kGemmBK);
+  for (long ks = 0; ks < n_k; ++ks) {
+    const int buf = static_cast<int>(ks & 1);
 #pragma unroll
-    for (int ks = 0; ks < kGemmBK / 16; ++ks) {
-      const int kk = ks * 16 + khalf;
+    for (int kk16 = 0; kk16 < kGemmBK / 16; ++kk16) {
+      const int kk = kk16 * 16 + khalf;
       bf16x8 fw[2], ft[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        fw[i] = *reinterpret_cast<const bf16x8*>(&ws[(wc * 64 + i * 32 + l32) * kGemmLD + kk]);
+        fw[i] = *reinterpret_cast<const bf16x8*>(&ws[buf][(wc * 64 + i * 32 + l32) * kGemmLD + kk]);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        ft[j] = *reinterpret_cast<const bf16x8*>(&as[(wt * 64 + j * 32 + l32) * kGemmLD + kk]);
+        ft[j] = *reinterpret_cast<const bf16x8*>(&as[buf][(wt * 64 + j * 32 + l32) * kGemmLD + kk]);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[i], ft[j], acc[i][j], 0, 0, 0);
     }
+    // Stage K slice ks+1 into the other buffer (last read in step ks-1, before the
+    // previous barrier), publish it, then fetch slice ks+2.
+    if (ks + 1 < n_k) store_tiles(buf ^ 1);
     __syncthreads();
-    if (more) {
-      store_tiles();
-      __syncthreads();
-    }
+    if (ks + 2 < n_k) load_tiles((ks + 2) * kGemmBK);
   }
 
   // Epilogue: lane holds token (l32) and features 8g + 4*(lane/32) + 0..3 of each 32-block.
@@ -213,8 +241,8 @@ hipError_t launch_qkv(const RowSource& src, long n, long dim, const uint16_t* w_
   a.k = out.k;
   a.v = out.v;
   a.to_cache = out.to_cache;
-  const dim3 grid(static_cast<unsigned>((a.ncols + kGemmBM - 1) / kGemmBM),
-                  static_cast<unsigned>((n + kGemmBN - 1) / kGemmBN));
+  const dim3 grid(static_cast<unsigned>((a.ncols + kGemmBM - 1) / kGemmBM *
+                                        ((n + kGemmBN - 1) / kGemmBN)));
   if (src.eps) {
     hipLaunchKernelGGL(qkv_gemm_kernel<kSrcRecover>, grid, dim3(256), 0, s, a);
   } else if (src.x_dtype == kDtypeF32) {

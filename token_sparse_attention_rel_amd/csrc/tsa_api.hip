@@ -13,6 +13,8 @@ namespace {
 using tsa::RowSource;
 
 constexpr int64_t kMaxRows = (int64_t{1} << 31) - 1;
+// Largest byte range a kernel addresses through one buffer resource (32-bit offsets).
+constexpr int64_t kMaxBufferBytes = (int64_t{1} << 31) - 1;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -135,6 +137,8 @@ tsa_status tsa_qkv_active(const void* x, int x_dtype, int64_t n_x_rows, const in
   if (dim <= 0 || dim % 64 != 0 || dim > (int64_t{1} << 20)) return TSA_ERR_SHAPE;
   if (!rows && n > n_x_rows) return TSA_ERR_SHAPE;
   if (out_is_cache && (n_cache < 0 || n_cache > kMaxRows)) return TSA_ERR_SHAPE;
+  // byte ranges of the token rows and of the weight must fit a 32-bit buffer range
+  if (n_x_rows * dim * 2 > kMaxBufferBytes || 3 * dim * dim * 2 > kMaxBufferBytes) return TSA_ERR_SHAPE;
   if (!aligned16(x) || !aligned16(w_qkv) || (q_out && !aligned16(q_out)) || !aligned16(k_out) ||
       !aligned16(v_out) || (eps && !aligned16(eps)) || (rows && !aligned4(rows)))
     return TSA_ERR_ALIGNMENT;
@@ -169,6 +173,7 @@ tsa_status tsa_sparse_query_attention(const tsa_bf16* q, const tsa_bf16* k_cache
   if (heads < 1 || heads > 4096) return TSA_ERR_SHAPE;
   if (n_q < 0 || n_q > kMaxRows || n_kv < 1 || n_kv > kMaxRows) return TSA_ERR_SHAPE;
   if (out_rows && (n_out < 0 || n_out > kMaxRows)) return TSA_ERR_SHAPE;
+  if (n_kv * heads * static_cast<int64_t>(head_dim) * 2 > kMaxBufferBytes) return TSA_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
       (out_rows && !aligned4(out_rows)) || (lse_out && !aligned4(lse_out)))
     return TSA_ERR_ALIGNMENT;
