@@ -41,6 +41,9 @@ def parse_args(argv=None):
     ap.add_argument("--cpu-sample-rows", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--attn-schedule", choices=("split", "tile"), default="split",
+                    help="attention: split the last, partly filled round of query tiles into key "
+                         "ranges (default) or run one workgroup per query tile throughout")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (HBM counter calibration)")
     return ap.parse_args(argv)
@@ -59,6 +62,13 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes_read_per_launch": 2 ** 30,
                       "copy_calibration_bytes_written_per_launch": 2 ** 30}), flush=True)
     return 0
+
+
+ATTN_KERNELS = {
+    False: "attention_kernel<128> (active queries x all cached K/V, fused scatter)",
+    True: "attention_split_kernel<128> + attention_merge_kernel<128> (active queries x all cached "
+          "K/V, fused scatter; timed together)",
+}
 
 
 def _src_hash(path):
@@ -151,12 +161,14 @@ def main(argv=None):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     inp = generate.step_inputs(cfg, args.seed)
-    layer = tsa.PrunedAttentionLayer(cfg.n, cfg.dim, cfg.heads, inp["w_qkv"].to(dev), device=dev)
+    layer = tsa.PrunedAttentionLayer(cfg.n, cfg.dim, cfg.heads, inp["w_qkv"].to(dev), device=dev,
+                                     split_attention=args.attn_schedule == "split")
     xp = inp["x_prev"].to(dev)
     xc = inp["x_cur"].to(dev)
     layer.init_cache(xp)
     k = cfg.n_active
     stream = torch.cuda.current_stream()
+    attn_ws = layer.attention_workspace(k)
 
     for _ in range(args.warmup):
         layer.step_topk(xc, xp, k)
@@ -174,7 +186,7 @@ def main(argv=None):
                        v_out=layer.v_cache, out_is_cache=True, n_cache=cfg.n)
         e[2].record(stream)
         tsa.sparse_query_attention(layer.q_a, layer.k_cache, layer.v_cache, k, cfg.heads,
-                                   cfg.head_dim, layer.out, out_rows=layer.idx)
+                                   cfg.head_dim, layer.out, out_rows=layer.idx, workspace=attn_ws)
         e[3].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -224,6 +236,8 @@ def main(argv=None):
             "head_dim": cfg.head_dim,
             "seed": args.seed,
         },
+        "attention_schedule": ("one workgroup per query tile, last round split into key ranges"
+                               if attn_ws is not None else "one workgroup per query tile"),
         "tokens_per_s": round(cfg.n / (ms_step * 1e-3), 1),
         "active_tokens_per_s": round(k / (ms_step * 1e-3), 1),
         "attn_tflops": round(achieved, 3),
@@ -235,7 +249,7 @@ def main(argv=None):
         "speedup_vs_dense": None if dense_ms is None else round(dense_ms / ms_step, 3),
         "roofline": {
             "bound": "mfma",
-            "kernel": "attention_kernel<128> (active queries x all cached K/V, fused scatter)",
+            "kernel": ATTN_KERNELS[attn_ws is not None],
             "achieved": round(achieved, 3),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",

@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define TSA_ABI_VERSION 1
+#define TSA_ABI_VERSION 2
 
 typedef uint16_t tsa_bf16;
 
@@ -193,14 +193,34 @@ tsa_status tsa_kv_cache_sync(const tsa_bf16* k_a, const tsa_bf16* v_a, const int
  *            otherwise [n_out, dim] with row r written to row out_rows[r]
  *            (this fuses the scatter, a8); other rows are not touched.
  *   lse_out  device f32 [heads, n_q] natural-log normaliser log sum_j exp(scale*s_j), or NULL.
+ *   workspace  device memory of at least tsa_attention_workspace_bytes() bytes for
+ *            the same n_q, n_kv, heads, head_dim on the current device, or NULL.
+ *            The query tiles (256 queries of one head for head_dim 128, 128 for
+ *            64) run one per workgroup.  With a workspace, when the last round
+ *            of tiles would leave compute units idle, each tile of that round
+ *            is instead cut into key ranges run by workgroups of their own; they
+ *            leave fp32 partials in the workspace and a second small kernel on
+ *            the same stream combines them.  NULL: no split.  Results agree to
+ *            rounding; the workspace keeps nothing between calls, and calls that
+ *            run concurrently need separate workspaces.
  * n_kv*heads*head_dim*2 must be below 2^31 bytes (32-bit buffer range of the cache).
- * Errors: INVALID_ARG, SHAPE, ALIGNMENT, HIP.
+ * Errors: INVALID_ARG, SHAPE, ALIGNMENT, WORKSPACE (workspace non-NULL and
+ * workspace_bytes below the required size), HIP.
  */
 tsa_status tsa_sparse_query_attention(const tsa_bf16* q, const tsa_bf16* k_cache,
                                       const tsa_bf16* v_cache, int64_t n_q, int64_t n_kv,
                                       int heads, int head_dim, float scale, tsa_bf16* out,
                                       const int32_t* out_rows, int64_t n_out, float* lse_out,
-                                      void* stream);
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace size for tsa_sparse_query_attention on the current device (the
+ * split depends on its compute-unit count); 0 when no split pays off or the
+ * shape is invalid.  Never more than 6 partials of 256 x 128 (head_dim 128) or
+ * 128 x 64 (head_dim 64) fp32 values plus 2 per query per resident workgroup:
+ * 207 MB for head_dim 128 on a 256-CU GPU.
+ */
+size_t tsa_attention_workspace_bytes(int64_t n_q, int64_t n_kv, int heads, int head_dim);
 
 /*
  * a8: outputs of the active tokens go back to token order; rows not listed

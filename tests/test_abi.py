@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(root):
 
 
 def test_version_and_status_strings():
-    assert tsa.abi_version() == 1
+    assert tsa.abi_version() == 2
     assert tsa.status_string(0) == "ok"
     assert "shape" in tsa.status_string(B.ERR_SHAPE)
     assert tsa.status_string(99) == "unknown status"
@@ -109,11 +109,12 @@ def test_qkv_validation():
 
 
 def attn(**kw):
-    a = dict(q=A, k=A, v=A, nq=16, nkv=64, heads=2, hd=64, scale=0.0, out=A, rows=None, nout=0, lse=None)
+    a = dict(q=A, k=A, v=A, nq=16, nkv=64, heads=2, hd=64, scale=0.0, out=A, rows=None, nout=0, lse=None,
+             ws=None, ws_bytes=0)
     a.update(kw)
     return lib().tsa_sparse_query_attention(a["q"], a["k"], a["v"], a["nq"], a["nkv"], a["heads"],
                                             a["hd"], a["scale"], a["out"], a["rows"], a["nout"],
-                                            a["lse"], None)
+                                            a["lse"], a["ws"], a["ws_bytes"], None)
 
 
 def test_attention_validation():
@@ -128,6 +129,13 @@ def test_attention_validation():
     assert attn(k=U) == B.ERR_ALIGNMENT
     assert attn(lse=A + 2) == B.ERR_ALIGNMENT
     assert attn(nkv=1 << 20, heads=8, hd=128) == B.ERR_SHAPE  # cache of 2 GiB
+    assert attn(ws=U, ws_bytes=1 << 20) == B.ERR_ALIGNMENT
+    assert attn(nq=0, ws=A, ws_bytes=0) == B.OK
+    f = lib()
+    assert f.tsa_attention_workspace_bytes(0, 64, 2, 64) == 0
+    assert f.tsa_attention_workspace_bytes(16, 64, 2, 96) == 0
+    assert f.tsa_attention_workspace_bytes(16, 64, 0, 128) == 0
+    assert f.tsa_attention_workspace_bytes(16, 0, 2, 128) == 0
 
 
 def test_row_mover_validation():

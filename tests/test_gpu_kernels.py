@@ -331,6 +331,70 @@ def test_attention_matches_oracle(n_q, n_kv, heads, hd):
     assert np.max(np.abs(G.host64(lse) - want_lse)) <= 1e-3 * max(1.0, np.abs(want_lse).max())
 
 
+# Split schedule: shapes whose last round of query tiles (256 queries for head_dim 128, 128
+# for 64) leaves a 256-CU GPU partly idle, ragged in queries and keys, so that tiles are cut
+# into key ranges and merged; fewer tiles than compute units (all tiles cut), tails of
+# a few tiles and of many, key counts of a few tiles and many.
+SPLIT_CASES = [(1100, 700, 60, 128), (300, 3000, 12, 64), (2000, 2085, 33, 128), (300, 5000, 3, 128),
+               (1030, 700, 52, 128), (1300, 1111, 60, 128), (129, 20000, 1, 128), (777, 4099, 4, 64)]
+
+
+@pytest.mark.parametrize("n_q,n_kv,heads,hd", SPLIT_CASES)
+def test_attention_split_matches_oracle(n_q, n_kv, heads, hd):
+    t = tsa()
+    ws_bytes = t.attention_workspace_bytes(n_q, n_kv, heads, hd)
+    assert ws_bytes > 0, "no split for this shape on this GPU"
+    g = torch.Generator().manual_seed(n_q + 3 * n_kv + heads)
+    dim = heads * hd
+    q = _randn_bf16(g, n_q, dim)
+    k = _randn_bf16(g, n_kv, dim)
+    v = _randn_bf16(g, n_kv, dim)
+    want, want_lse = ref.attention(G.host64(q), G.host64(k), G.host64(v), heads, return_lse=True)
+    qd, kd, vd = G.dev(q), G.dev(k), G.dev(v)
+    ws = torch.full((ws_bytes,), 0xFF, dtype=torch.uint8, device="cuda")  # NaN bytes
+    lse = torch.empty(heads, n_q, dtype=torch.float32, device="cuda")
+    for rep in range(2):  # the workspace keeps the first call's partials
+        out = torch.empty(n_q, dim, dtype=torch.bfloat16, device="cuda")
+        t.sparse_query_attention(qd, kd, vd, n_q, heads, hd, out, lse_out=lse, workspace=ws)
+        G.assert_close(G.host64(out), want, f"split attn {n_q}x{n_kv} h{heads} d{hd} call {rep}")
+        assert np.max(np.abs(G.host64(lse) - want_lse)) <= 1e-3 * max(1.0, np.abs(want_lse).max())
+    # without a workspace: one workgroup per tile, the same result to rounding
+    o_plain = torch.empty(n_q, dim, dtype=torch.bfloat16, device="cuda")
+    t.sparse_query_attention(qd, kd, vd, n_q, heads, hd, o_plain)
+    G.assert_close(G.host64(o_plain), want, "plain path")
+    with pytest.raises(t.TsaError):
+        t.sparse_query_attention(qd, kd, vd, n_q, heads, hd, out, workspace=ws[:ws_bytes - 16])
+
+
+def test_attention_split_fused_scatter():
+    t = tsa()
+    g = torch.Generator().manual_seed(21)
+    n, heads, hd = 3000, 64, 128
+    dim = heads * hd
+    rows = np.sort(np.random.default_rng(5).choice(n, 1111, replace=False)).astype(np.int32)
+    ws = torch.empty(t.attention_workspace_bytes(rows.size, n, heads, hd), dtype=torch.uint8, device="cuda")
+    assert ws.numel() > 0
+    q = _randn_bf16(g, rows.size, dim)
+    k = _randn_bf16(g, n, dim)
+    v = _randn_bf16(g, n, dim)
+    base = _randn_bf16(g, n, dim)
+    out = G.dev(base)
+    t.sparse_query_attention(G.dev(q), G.dev(k), G.dev(v), rows.size, heads, hd, out,
+                             out_rows=G.dev(torch.from_numpy(rows)), workspace=ws)
+    oh = out.cpu()
+    others = np.setdiff1d(np.arange(n), rows)
+    assert torch.equal(oh[others], base[others])
+    want = ref.attention(G.host64(q), G.host64(k), G.host64(v), heads)
+    G.assert_close(G.host64(oh)[rows], want, "split fused scatter")
+
+
+def test_attention_no_split_when_last_round_is_full():
+    """A tile count that is a multiple of the resident workgroups needs no split."""
+    t = tsa()
+    assert t.attention_workspace_bytes(256 * 256, 4096, 1, 128) == 0
+    assert t.attention_workspace_bytes(100, 5000, 3, 128) > 0
+
+
 def test_attention_scaled_inputs_and_scale_argument():
     """Large logits (sharp softmax) and an explicit scale."""
     t = tsa()
@@ -394,4 +458,13 @@ def test_attention_deterministic():
     o2 = torch.empty_like(o1)
     t.sparse_query_attention(q, k, v, n_q, heads, hd, o1)
     t.sparse_query_attention(q, k, v, n_q, heads, hd, o2)
+    assert torch.equal(o1, o2)
+    # split schedule: the same cut points every call, so also bitwise repeatable
+    n_q, heads = 1100, 60
+    q, k, v = (G.dev(_randn_bf16(g, s, heads * hd)) for s in (n_q, 700, 700))
+    ws = torch.empty(t.attention_workspace_bytes(n_q, 700, heads, hd), dtype=torch.uint8, device="cuda")
+    o1 = torch.empty(n_q, heads * hd, dtype=torch.bfloat16, device="cuda")
+    o2 = torch.empty_like(o1)
+    t.sparse_query_attention(q, k, v, n_q, heads, hd, o1, workspace=ws)
+    t.sparse_query_attention(q, k, v, n_q, heads, hd, o2, workspace=ws)
     assert torch.equal(o1, o2)

@@ -19,6 +19,7 @@ from ._binding import (
     TsaError,
     abi_version,
     assign_groups,
+    attention_workspace_bytes,
     gather_rows,
     kv_cache_sync,
     lib,
@@ -36,7 +37,7 @@ lib()  # load now: fail loudly when the HIP library is missing
 
 __all__ = [
     "BF16", "F32", "SCORE_ABS_L1", "SCORE_REL_L1", "SELECT_MASK", "SELECT_SCHEDULE",
-    "SELECT_THRESHOLD", "SELECT_TOPK", "TsaError", "abi_version", "assign_groups", "gather_rows",
+    "SELECT_THRESHOLD", "SELECT_TOPK", "TsaError", "abi_version", "assign_groups", "attention_workspace_bytes", "gather_rows",
     "kv_cache_sync", "lib", "lib_path", "qkv_active", "scatter_out", "select_active",
     "select_workspace_bytes", "sparse_query_attention", "status_string",
     "PrunedAttentionLayer", "hsa_active_count",

@@ -40,7 +40,8 @@ _SIGNATURES = {
                               _vp, _i64, _f32, _vp]),
     "tsa_kv_cache_sync": (_int, [_vp, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _vp]),
     "tsa_sparse_query_attention": (_int, [_vp, _vp, _vp, _i64, _i64, _int, _int, _f32, _vp, _vp,
-                                          _i64, _vp, _vp]),
+                                          _i64, _vp, _vp, _size, _vp]),
+    "tsa_attention_workspace_bytes": (_size, [_i64, _i64, _int, _int]),
     "tsa_scatter_out": (_int, [_vp, _vp, _i64, _vp, _i64, _i64, _vp]),
     "tsa_gather_rows": (_int, [_vp, _i64, _vp, _i64, _i64, _vp, _i64, _f32, _vp, _vp]),
 }
@@ -179,14 +180,21 @@ def kv_cache_sync(k_a, v_a, rows, n, k_cache, v_cache, stream=None):
     _check("tsa_kv_cache_sync", st)
 
 
+def attention_workspace_bytes(n_q, n_kv, heads, head_dim):
+    """tsa_attention_workspace_bytes (current device)."""
+    return int(lib().tsa_attention_workspace_bytes(int(n_q), int(n_kv), int(heads), int(head_dim)))
+
+
 def sparse_query_attention(q, k_cache, v_cache, n_q, heads, head_dim, out, *, out_rows=None,
-                           scale=0.0, lse_out=None, stream=None):
-    """a7 (+a8 when out_rows is given) (tsa_sparse_query_attention)."""
+                           scale=0.0, lse_out=None, workspace=None, stream=None):
+    """a7 (+a8 when out_rows is given) (tsa_sparse_query_attention).  ``workspace``:
+    a device tensor of at least attention_workspace_bytes() bytes, or None."""
     n_out = out.shape[0]
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = lib().tsa_sparse_query_attention(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), int(n_q), int(k_cache.shape[0]), int(heads),
         int(head_dim), float(scale), _ptr(out), _ptr(out_rows), int(n_out), _ptr(lse_out),
-        _stream(stream))
+        _ptr(workspace), ws_bytes, _stream(stream))
     _check("tsa_sparse_query_attention", st)
 
 

@@ -21,6 +21,7 @@
 // are exactly the B operand it must supply, provided the V^T operand uses
 // the same key order inside each 16-key chunk -- which the transposing LDS
 // reads of row-major V deliver directly.  No probabilities travel through LDS.
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -29,6 +30,13 @@
 namespace tsa {
 
 constexpr int kAttnBN = 32;  // keys per tile
+constexpr int kMaxDevices = 64;
+// Split schedule limits: at most kMaxPieces pieces per tile, each at least
+// kMinPieceTiles key tiles long, and at most kMaxPieceSlots pieces per resident
+// workgroup in total (this bounds the workspace).
+constexpr int kMaxPieces = 64;
+constexpr int kMinPieceTiles = 4;
+constexpr int kMaxPieceSlots = 6;
 
 // Waves per workgroup (32 queries each): 8 for head_dim 128, so every thread
 // stages one 16-byte chunk of K and of V per tile and one K/V tile in LDS feeds
@@ -75,8 +83,18 @@ constexpr int kBufferRsrcFlags = 0x00020000;
 template <bool B>
 using Flag = std::integral_constant<bool, B>;
 
+// Partial result of one segment, laid out as the registers hold it (lane fastest):
+// O^T accumulators [wave][NDB*16][64], then the shift m and the sum l [wave][64].
 template <int HD>
-__global__ __launch_bounds__(64 * attn_waves<HD>(), 2) void attention_kernel(AttnArgs a) {
+constexpr long attn_piece_floats() { return attn_waves<HD>() * 64L * (HD / 32 * 16 + 2); }
+
+// Keys [t0*BN, t1*BN) of query tile `tile` (head-major numbering).  part == nullptr:
+// normalise and write the bf16 output rows (+ LSE); otherwise write the partial
+// (unnormalised O, shift, sum) to `part` for a later merge.  ks / vs are the two
+// LDS buffers of K and V tiles.
+template <int HD>
+__device__ __forceinline__ void attend_segment(const AttnArgs& a, uint16_t* ks_base, uint16_t* vs_base,
+                                               long tile, long t0, long t1, float* part) {
   constexpr int BN = kAttnBN;
   constexpr int NT = 64 * attn_waves<HD>();  // threads
   constexpr int BM = 32 * attn_waves<HD>();  // queries per workgroup
@@ -91,11 +109,11 @@ __global__ __launch_bounds__(64 * attn_waves<HD>(), 2) void attention_kernel(Att
   constexpr int NCH = BN * CPR / NT;   // chunks per thread per tile (K and V each)
   static_assert(NCH >= 1, "tile too small for the workgroup");
 
-  __shared__ __align__(16) uint16_t ks[2][BN * LDK];
-  __shared__ __align__(16) uint16_t vs[2][BN * LDV];
+  // Buffer i of each pair; plain offsets from the LDS base keep every access an LDS one.
+  auto ks = [&](int i) { return ks_base + i * (BN * LDK); };
+  auto vs = [&](int i) { return vs_base + i * (BN * LDV); };
 
   const long n_qt = (a.n_q + BM - 1) / BM;
-  const long tile = xcd_remap(blockIdx.x, n_qt * a.heads);
   const int head = static_cast<int>(tile / n_qt);
   const long qt = tile - static_cast<long>(head) * n_qt;
 
@@ -190,28 +208,28 @@ __global__ __launch_bounds__(64 * attn_waves<HD>(), 2) void attention_kernel(Att
   const float c = a.scale_log2;
   const long n_t = (n_kv + BN - 1) / BN;
 
-  // Prologue: K tiles 0 and 1 in LDS, S of tile 0; registers hold K(2) and V(0).
+  // Prologue: K tiles t0 and t0+1 in LDS, S of tile t0; registers hold K(t0+2), V(t0).
   u32x4 kr[NCH], vr[NCH];
-  gload(kr, krs, 0);
-  sstore(ks[0], k_lds, kr);
-  gload(kr, krs, BN);
-  sstore(ks[1], k_lds, kr);
+  gload(kr, krs, t0 * BN);
+  sstore(ks(0), k_lds, kr);
+  gload(kr, krs, (t0 + 1) * BN);
+  sstore(ks(1), k_lds, kr);
   __syncthreads();
-  gload(kr, krs, 2 * BN);
-  gload(vr, vrs, 0);
-  f32x16 s_cur = qk(ks[0]);
-  mask_tail(s_cur, 0);
-  __syncthreads();  // every wave is done with K(0) before K(2) overwrites it
+  gload(kr, krs, (t0 + 2) * BN);
+  gload(vr, vrs, t0 * BN);
+  f32x16 s_cur = qk(ks(0));
+  mask_tail(s_cur, t0 * BN);
+  __syncthreads();  // every wave is done with K(t0) before K(t0+2) overwrites it
 
   bf16x8 p_prev[2];
   // Iteration t: MFMA work PV(t-1) and QK(t+1) interleaved with the softmax of
   // tile t on the VALU; then stage V(t) and K(t+2) and fetch V(t+1) and K(t+3).
   // A buffer is rewritten only after the barrier that follows its last read.
   auto iteration = [&](long t, auto has_prev, auto has_next, auto may_mask) {
-    const int b = static_cast<int>(t & 1);
+    const int b = static_cast<int>((t - t0) & 1);
     f32x16 s_next;
-    if constexpr (decltype(has_prev)::value) pv(vs[b ^ 1], p_prev);
-    if constexpr (decltype(has_next)::value) s_next = qk(ks[b ^ 1]);
+    if constexpr (decltype(has_prev)::value) pv(vs(b ^ 1), p_prev);
+    if constexpr (decltype(has_next)::value) s_next = qk(ks(b ^ 1));
 
     float mx = -__builtin_inff();
 #pragma unroll
@@ -242,8 +260,8 @@ __global__ __launch_bounds__(64 * attn_waves<HD>(), 2) void attention_kernel(Att
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (decltype(may_mask)::value) mask_tail(s_next, (t + 1) * BN);
 
-    sstore(vs[b], v_lds, vr);
-    sstore(ks[b], k_lds, kr);
+    sstore(vs(b), v_lds, vr);
+    sstore(ks(b), k_lds, kr);
     __syncthreads();
     gload(vr, vrs, (t + 1) * BN);
     gload(kr, krs, (t + 3) * BN);
@@ -260,17 +278,30 @@ __global__ __launch_bounds__(64 * attn_waves<HD>(), 2) void attention_kernel(Att
     }
   };
 
-  if (n_t == 1) {
-    iteration(0, Flag<false>{}, Flag<false>{}, Flag<false>{});
+  // Only the last key tile of the cache can be partial, so only the iterations
+  // whose next tile may be it carry the masking code.
+  if (t1 - t0 == 1) {
+    iteration(t0, Flag<false>{}, Flag<false>{}, Flag<false>{});
   } else {
-    iteration(0, Flag<false>{}, Flag<true>{}, Flag<true>{});
-    for (long t = 1; t + 2 < n_t; ++t) iteration(t, Flag<true>{}, Flag<true>{}, Flag<false>{});
-    if (n_t > 2) iteration(n_t - 2, Flag<true>{}, Flag<true>{}, Flag<true>{});
-    iteration(n_t - 1, Flag<true>{}, Flag<false>{}, Flag<false>{});
+    iteration(t0, Flag<false>{}, Flag<true>{}, Flag<true>{});
+    for (long t = t0 + 1; t + 2 < t1; ++t) iteration(t, Flag<true>{}, Flag<true>{}, Flag<false>{});
+    if (t1 - t0 > 2) iteration(t1 - 2, Flag<true>{}, Flag<true>{}, Flag<true>{});
+    iteration(t1 - 1, Flag<true>{}, Flag<false>{}, Flag<false>{});
   }
-  pv(vs[(n_t - 1) & 1], p_prev);
+  pv(vs((t1 - 1 - t0) & 1), p_prev);
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if (part) {
+    float* pw = part + static_cast<long>(wave) * (NDB * 16 * 64);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pw[(db * 16 + r) * 64 + lane] = acc[db][r];
+    float* ml = part + attn_waves<HD>() * 64L * NDB * 16;
+    ml[wave * 64 + lane] = m_run;
+    ml[attn_waves<HD>() * 64 + wave * 64 + lane] = l_tot;
+    return;
+  }
   if (qvalid) {
     const float inv = 1.0f / l_tot;
     const long orow = a.out_rows ? static_cast<long>(a.out_rows[qrow]) : qrow;
@@ -287,9 +318,191 @@ __global__ __launch_bounds__(64 * attn_waves<HD>(), 2) void attention_kernel(Att
   }
 }
 
+template <int HD>
+__global__ __launch_bounds__(64 * attn_waves<HD>(), 2) void attention_kernel(AttnArgs a) {
+  __shared__ __align__(16) uint16_t ks[2 * kAttnBN * (HD + 8)];
+  __shared__ __align__(16) uint16_t vs[2 * kAttnBN * (HD + 32)];
+  const long n_qt = (a.n_q + 32 * attn_waves<HD>() - 1) / (32 * attn_waves<HD>());
+  const long tile = xcd_remap(blockIdx.x, n_qt * a.heads);
+  attend_segment<HD>(a, ks, vs, tile, 0, (a.n_kv + kAttnBN - 1) / kAttnBN, nullptr);
+}
+
+// Split schedule for the last, partly filled round of query tiles.  With C
+// resident workgroups and T tiles, the first R = floor(T / C) * C tiles run
+// whole, one workgroup each, as in attention_kernel.  Each of the r = T - R
+// remaining tiles is cut into kp key ranges (pieces) run by workgroups of their
+// own, which write fp32 partials (unnormalised O, shift, sum) to the workspace;
+// attention_merge_kernel combines them.  Pieces are numbered key-range-major
+// and dealt to XCDs in contiguous runs, so the workgroups resident on one XCD
+// at a time read the same key range of the same head and share its L2.
+template <int HD>
+__global__ __launch_bounds__(64 * attn_waves<HD>(), 2) void attention_split_kernel(AttnArgs a, float* ws,
+                                                                                   long full, long tail,
+                                                                                   int kp) {
+  __shared__ __align__(16) uint16_t ks[2 * kAttnBN * (HD + 8)];
+  __shared__ __align__(16) uint16_t vs[2 * kAttnBN * (HD + 32)];
+  const long n_t = (a.n_kv + kAttnBN - 1) / kAttnBN;
+  const long b = blockIdx.x;
+  if (b < full) {
+    attend_segment<HD>(a, ks, vs, xcd_remap(b, full), 0, n_t, nullptr);
+    return;
+  }
+  const long p = xcd_remap(b - full, tail * kp);
+  const long j = p / tail, i = p - j * tail;
+  attend_segment<HD>(a, ks, vs, full + i, j * n_t / kp, (j + 1) * n_t / kp,
+                     ws + (i * kp + j) * attn_piece_floats<HD>());
+}
+
+// One workgroup per cut tile: O = sum_j w_j O_j / sum_j w_j l_j with
+// w_j = 2^(m_j - max_j m_j); bf16 rows (+ LSE) written as attention_kernel does.
+template <int HD>
+__global__ __launch_bounds__(64 * attn_waves<HD>()) void attention_merge_kernel(AttnArgs a, const float* ws,
+                                                                                 long full, int kp) {
+  constexpr int NDB = HD / 32;
+  constexpr int NW = attn_waves<HD>();
+  constexpr long piece = attn_piece_floats<HD>();
+  const long n_qt = (a.n_q + 32 * NW - 1) / (32 * NW);
+  const long tile = full + blockIdx.x;
+  const int head = static_cast<int>(tile / n_qt);
+  const long qt = tile - static_cast<long>(head) * n_qt;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const long qrow = qt * 32 * NW + wave * 32 + l32;
+  if (qrow >= a.n_q) return;
+  const float* p0 = ws + static_cast<long>(blockIdx.x) * kp * piece;
+  const long mo = NW * 64L * NDB * 16;  // offset of the shifts; the sums follow
+  const int ml = wave * 64 + lane;
+  float m = -__builtin_inff();
+  for (int j = 0; j < kp; ++j) m = fmaxf(m, p0[j * piece + mo + ml]);
+  float l = 0.f;
+  for (int j = 0; j < kp; ++j)
+    l = fmaf(p0[j * piece + mo + NW * 64 + ml], __builtin_amdgcn_exp2f(p0[j * piece + mo + ml] - m), l);
+  const float inv = 1.0f / l;
+  const long D = static_cast<long>(a.heads) * HD;
+  const long orow = a.out_rows ? static_cast<long>(a.out_rows[qrow]) : qrow;
+  uint16_t* op = a.out + orow * D + head * HD + 4 * hi;
+  const float* acc = p0 + static_cast<long>(wave) * (NDB * 16 * 64) + lane;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      float o[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < kp; ++j) {
+        const float w = __builtin_amdgcn_exp2f(p0[j * piece + mo + ml] - m);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = fmaf(acc[j * piece + (db * 16 + 4 * g + e) * 64], w, o[e]);
+      }
+      *reinterpret_cast<u32x2*>(op + db * 32 + g * 8) =
+          u32x2{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)};
+    }
+  if (a.lse && hi == 0) a.lse[head * a.n_q + qrow] = (m + __log2f(l)) * 0.69314718055994531f;
+}
+
+namespace {
+
+// Workgroups of attention_split_kernel resident at once on the current device:
+// compute units times resident workgroups per unit.  Cached per device.
+template <int HD>
+long resident_ctas() {
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < kMaxDevices) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attention_split_kernel<HD>,
+                                                   64 * attn_waves<HD>(), 0) != hipSuccess)
+    return 0;
+  const int c = cus * (per_cu > 0 ? per_cu : 1);
+  if (dev < kMaxDevices) cache[dev].store(c, std::memory_order_relaxed);
+  return c;
+}
+
+template <int HD>
+long query_tiles(long n_q, int heads) {
+  constexpr long bm = 32 * attn_waves<HD>();
+  return (n_q + bm - 1) / bm * heads;
+}
+
+struct SplitPlan {
+  long full = 0;  // tiles run whole
+  long tail = 0;  // tiles cut into pieces
+  int kp = 1;     // pieces per cut tile (1: no split)
+};
+
+// Cost model, in key-tile steps of one workgroup at full load.  Whole tiles in a
+// partly filled last round run faster than at full load (measured on MI355X:
+// about 0.79 + 0.1 x the full-load time with a fraction x of the workgroup slots
+// busy), so that round costs n_t (0.79 + 0.1 r / C).  Split, it costs rounds of
+// pieces of n_t / k steps plus about 3 steps of pipeline fill each, at the
+// full-load rate.  The split is taken only when it saves at least 7%.
+template <int HD>
+SplitPlan split_plan(long n_q, long n_kv, int heads) {
+  SplitPlan sp;
+  const long c = resident_ctas<HD>();
+  const long tiles = query_tiles<HD>(n_q, heads);
+  const long n_t = (n_kv + kAttnBN - 1) / kAttnBN;
+  if (c < 1) return sp;
+  const long r = tiles % c;
+  if (r == 0) return sp;
+  const double whole = static_cast<double>(n_t) * (0.79 + 0.1 * static_cast<double>(r) / c);
+  double best = whole;
+  int best_k = 1;
+  for (int k = 2; k <= kMaxPieces && static_cast<long>(k) * kMinPieceTiles <= n_t &&
+                  r * k <= kMaxPieceSlots * c;
+       ++k) {
+    const double cost = static_cast<double>((r * k + c - 1) / c) * (static_cast<double>(n_t) / k + 3.0);
+    if (cost < best) {
+      best = cost;
+      best_k = k;
+    }
+  }
+  if (best_k == 1 || best > 0.93 * whole) return sp;
+  sp.full = tiles - r;
+  sp.tail = r;
+  sp.kp = best_k;
+  return sp;
+}
+
+template <int HD>
+size_t split_bytes(const SplitPlan& sp) {
+  return static_cast<size_t>(sp.tail) * sp.kp * attn_piece_floats<HD>() * sizeof(float);
+}
+
+template <int HD>
+hipError_t launch_hd(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t s) {
+  const SplitPlan sp = ws ? split_plan<HD>(a.n_q, a.n_kv, a.heads) : SplitPlan{};
+  const dim3 block(64 * attn_waves<HD>());
+  if (sp.kp == 1) {
+    hipLaunchKernelGGL(attention_kernel<HD>, dim3(static_cast<unsigned>(query_tiles<HD>(a.n_q, a.heads))),
+                       block, 0, s, a);
+    return hipGetLastError();
+  }
+  if (ws_bytes < split_bytes<HD>(sp)) return hipErrorInvalidValue;
+  float* w = static_cast<float*>(ws);
+  hipLaunchKernelGGL(attention_split_kernel<HD>, dim3(static_cast<unsigned>(sp.full + sp.tail * sp.kp)),
+                     block, 0, s, a, w, sp.full, sp.tail, sp.kp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attention_merge_kernel<HD>, dim3(static_cast<unsigned>(sp.tail)), block, 0, s, a,
+                     static_cast<const float*>(w), sp.full, sp.kp);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t attention_workspace_bytes(long n_q, long n_kv, int heads, int head_dim) {
+  return head_dim == 128 ? split_bytes<128>(split_plan<128>(n_q, n_kv, heads))
+                         : split_bytes<64>(split_plan<64>(n_q, n_kv, heads));
+}
+
 hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, long n_q,
                             long n_kv, int heads, int head_dim, float scale, uint16_t* out,
-                            const int* out_rows, float* lse, hipStream_t s) {
+                            const int* out_rows, float* lse, void* ws, size_t ws_bytes,
+                            hipStream_t s) {
   AttnArgs a;
   a.q = q;
   a.k = k;
@@ -301,16 +514,7 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t
   a.out = out;
   a.out_rows = out_rows;
   a.lse = lse;
-  if (head_dim == 128) {
-    constexpr int bm = 32 * attn_waves<128>();
-    const dim3 grid(static_cast<unsigned>((n_q + bm - 1) / bm * heads));
-    hipLaunchKernelGGL(attention_kernel<128>, grid, dim3(64 * attn_waves<128>()), 0, s, a);
-  } else {
-    constexpr int bm = 32 * attn_waves<64>();
-    const dim3 grid(static_cast<unsigned>((n_q + bm - 1) / bm * heads));
-    hipLaunchKernelGGL(attention_kernel<64>, grid, dim3(64 * attn_waves<64>()), 0, s, a);
-  }
-  return hipGetLastError();
+  return head_dim == 128 ? launch_hd<128>(a, ws, ws_bytes, s) : launch_hd<64>(a, ws, ws_bytes, s);
 }
 
 }  // namespace tsa

@@ -49,8 +49,13 @@ hipError_t launch_qkv(const RowSource& src, long n, long dim, const uint16_t* w_
                       const QkvOut& out, hipStream_t s);
 
 // attention.hip
+// ws == nullptr: one workgroup per query tile.  Otherwise the split schedule of
+// the last round when it pays, with ws of at least attention_workspace_bytes()
+// bytes (hipErrorInvalidValue if smaller).
+size_t attention_workspace_bytes(long n_q, long n_kv, int heads, int head_dim);
 hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, long n_q,
                             long n_kv, int heads, int head_dim, float scale, uint16_t* out,
-                            const int* out_rows, float* lse, hipStream_t s);
+                            const int* out_rows, float* lse, void* ws, size_t ws_bytes,
+                            hipStream_t s);
 
 }  // namespace tsa

@@ -2,7 +2,8 @@
 //
 // Every entry point validates all arguments before enqueuing anything, so a
 // rejected call writes nothing.  Nothing here allocates, frees or
-// synchronises; nothing keeps state between calls.
+// synchronises; the only state kept between calls is a per-device cache of
+// the attention kernel's resident workgroup count.
 #include <math.h>
 
 #include "../../include/tsa.h"
@@ -166,7 +167,7 @@ tsa_status tsa_sparse_query_attention(const tsa_bf16* q, const tsa_bf16* k_cache
                                       const tsa_bf16* v_cache, int64_t n_q, int64_t n_kv,
                                       int heads, int head_dim, float scale, tsa_bf16* out,
                                       const int32_t* out_rows, int64_t n_out, float* lse_out,
-                                      void* stream) {
+                                      void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k_cache || !v_cache || !out) return TSA_ERR_INVALID_ARG;
   if (isnan(scale) || isinf(scale)) return TSA_ERR_INVALID_ARG;
   if (head_dim != 64 && head_dim != 128) return TSA_ERR_SHAPE;
@@ -175,12 +176,23 @@ tsa_status tsa_sparse_query_attention(const tsa_bf16* q, const tsa_bf16* k_cache
   if (out_rows && (n_out < 0 || n_out > kMaxRows)) return TSA_ERR_SHAPE;
   if (n_kv * heads * static_cast<int64_t>(head_dim) * 2 > kMaxBufferBytes) return TSA_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
-      (out_rows && !aligned4(out_rows)) || (lse_out && !aligned4(lse_out)))
+      (out_rows && !aligned4(out_rows)) || (lse_out && !aligned4(lse_out)) ||
+      (workspace && !aligned16(workspace)))
     return TSA_ERR_ALIGNMENT;
   if (n_q == 0) return TSA_OK;
+  if (workspace && workspace_bytes < tsa::attention_workspace_bytes(n_q, n_kv, heads, head_dim))
+    return TSA_ERR_WORKSPACE;
   const float sc = scale > 0.f ? scale : 1.0f / sqrtf(static_cast<float>(head_dim));
   return from_hip(tsa::launch_attention(q, k_cache, v_cache, n_q, n_kv, heads, head_dim, sc, out,
-                                        out_rows, lse_out, as_stream(stream)));
+                                        out_rows, lse_out, workspace, workspace_bytes,
+                                        as_stream(stream)));
+}
+
+size_t tsa_attention_workspace_bytes(int64_t n_q, int64_t n_kv, int heads, int head_dim) {
+  if ((head_dim != 64 && head_dim != 128) || heads < 1 || heads > 4096 || n_q < 1 || n_q > kMaxRows ||
+      n_kv < 1 || n_kv > kMaxRows)
+    return 0;
+  return tsa::attention_workspace_bytes(n_q, n_kv, heads, head_dim);
 }
 
 tsa_status tsa_scatter_out(const tsa_bf16* o_a, const int32_t* rows, int64_t n, tsa_bf16* out,

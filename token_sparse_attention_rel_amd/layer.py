@@ -17,7 +17,8 @@ from . import _binding as B
 
 
 class PrunedAttentionLayer:
-    def __init__(self, n: int, dim: int, heads: int, w_qkv: torch.Tensor, device="cuda"):
+    def __init__(self, n: int, dim: int, heads: int, w_qkv: torch.Tensor, device="cuda", *,
+                 split_attention: bool = True):
         if dim % heads:
             raise ValueError("dim must be a multiple of heads")
         self.n, self.dim, self.heads = n, dim, heads
@@ -42,6 +43,21 @@ class PrunedAttentionLayer:
         self._o_a = None
         ws = B.select_workspace_bytes(n)
         self.workspace = torch.empty(max(ws, 16) + n, dtype=torch.uint8, device=dev)
+        # partials of the attention's split last round, grown on demand
+        self.split_attention = split_attention
+        self._attn_ws = torch.empty(0, dtype=torch.uint8, device=dev)
+
+    def attention_workspace(self, n_q: int):
+        """Workspace for attention of n_q active queries over the cache (None: no split)."""
+        if not self.split_attention:
+            return None
+        with torch.cuda.device(self.device):
+            need = B.attention_workspace_bytes(n_q, self.n, self.heads, self.head_dim)
+        if need == 0:
+            return None
+        if self._attn_ws.numel() < need:
+            self._attn_ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        return self._attn_ws
 
     # ---------------------------------------------------------------- state
 
@@ -86,14 +102,16 @@ class PrunedAttentionLayer:
             B.qkv_active(x_cur, idx, n_active, self.w_qkv, q_out=self.q_a, k_out=self.k_cache,
                          v_out=self.v_cache, out_is_cache=True, n_cache=self.n, stream=stream)
             B.sparse_query_attention(self.q_a, self.k_cache, self.v_cache, n_active, self.heads,
-                                     self.head_dim, self.out, out_rows=idx, stream=stream)
+                                     self.head_dim, self.out, out_rows=idx,
+                                     workspace=self.attention_workspace(n_active), stream=stream)
         else:
             k_a, v_a, o_a = self._compact_bufs()
             B.qkv_active(x_cur, idx, n_active, self.w_qkv, q_out=self.q_a, k_out=k_a, v_out=v_a,
                          stream=stream)
             B.kv_cache_sync(k_a, v_a, idx, n_active, self.k_cache, self.v_cache, stream=stream)
             B.sparse_query_attention(self.q_a, self.k_cache, self.v_cache, n_active, self.heads,
-                                     self.head_dim, o_a, stream=stream)
+                                     self.head_dim, o_a, workspace=self.attention_workspace(n_active),
+                                     stream=stream)
             B.scatter_out(o_a, idx, n_active, self.out, stream=stream)
 
     def step_topk(self, x_cur, x_ref, k: int, *, fused=True, stream=None) -> None:
@@ -122,7 +140,8 @@ class PrunedAttentionLayer:
                          src_row_offset=hw, sigma=sigma, stream=stream)
         if k:
             B.sparse_query_attention(self.q_a, self.k_cache, self.v_cache, k, self.heads,
-                                     self.head_dim, self.out, out_rows=self.idx, stream=stream)
+                                     self.head_dim, self.out, out_rows=self.idx,
+                                     workspace=self.attention_workspace(k), stream=stream)
 
 
 def hsa_active_count(group_counts, group_periods, step: int) -> int:
