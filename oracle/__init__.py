@@ -16,11 +16,12 @@ summaries of the papers):
 * HSA -- "Resumen Técnico: Asignación de Pasos Heterogénea (HSA) para la
   Generación Eficiente de Video" (gist.science/es/paper/2605.06892):
   §2.1 token partition and schedule, §2.2 KV-cache synchronisation,
-  §2.3 cached Euler update.
+  §2.3 cached Euler update, §2.4 phase-aware cache window.
 * LIPAR -- "Training-free Latent Inter-Frame Pruning with Attention Recovery"
   (gist.science/es/paper/2603.05811 and gist.science/nl/paper/2603.05811):
-  §2.B latent inter-frame pruning, §2.C attention recovery (noise-aware
-  duplication), Dutch §2.D restoration.
+  §2.B latent inter-frame pruning (with its short- and long-term change
+  mask), §2.C attention recovery (noise-aware duplication), Dutch §2.D
+  restoration.
 
 Parity status of each function is stated in its docstring; the end-to-end
 layer is pinned only through its pinned steps (there is no worked example on

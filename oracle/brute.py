@@ -8,6 +8,7 @@ in both.  Only for tiny inputs (N <= 64 tokens).
 from __future__ import annotations
 
 import math
+import struct
 
 
 def bf16(x: float) -> float:
@@ -118,4 +119,80 @@ def periods_by_rank(s, counts, periods):
         for i in ranked[pos:pos + c]:
             out[i] = p
         pos += c
+    return out
+
+
+def f32(x: float) -> float:
+    """Nearest float32, ties to even (the struct module's conversion)."""
+    return struct.unpack("f", struct.pack("f", x))[0]
+
+
+def euler(x, v, dt):
+    """x + dt * v per element, the exact value rounded once to float32 (fsum keeps it exact)."""
+    return [[f32(math.fsum([a, dt * b])) for a, b in zip(xr, vr)] for xr, vr in zip(x, v)]
+
+
+def hsa_run(x0, w_qkv, heads, periods, sigmas, window):
+    """The sampling loop: dense steps in the window, schedule elsewhere, Euler update after each."""
+    steps = len(sigmas) - 1
+    n, d = len(x0), len(x0[0])
+    x = [list(r) for r in x0]
+    k_cache = [[0.0] * d for _ in range(n)]
+    v_cache = [[0.0] * d for _ in range(n)]
+    v_hat = [[0.0] * d for _ in range(n)]
+    hist = []
+    for i in range(steps):
+        dense = i < window or i >= steps - window
+        idx = [t for t in range(n) if dense or i % periods[t] == 0]
+        xa = [x[t] for t in idx]
+        q = project(xa, w_qkv, "q")
+        ka = project(xa, w_qkv, "k")
+        va = project(xa, w_qkv, "v")
+        for r, t in enumerate(idx):
+            k_cache[t] = list(ka[r])
+            v_cache[t] = list(va[r])
+        o = attention(q, k_cache, v_cache, heads)
+        for r, t in enumerate(idx):
+            v_hat[t] = list(o[r])
+        dt = f32(sigmas[i + 1] - sigmas[i])
+        x = euler(x, v_hat, dt)
+        hist.append({"idx": idx, "v_hat": [list(r) for r in v_hat], "x": [list(r) for r in x]})
+    return hist
+
+
+def lif_mask(x, frames, hw, tau_short, tau_long, relative=False):
+    """Frame-by-frame scan per location with short- and long-term L1 changes."""
+    def change(a, b):
+        num = math.fsum(abs(p - r) for p, r in zip(a, b))
+        if not relative:
+            return num
+        den = math.fsum(abs(r) for r in b)
+        if den == 0.0:
+            return 0.0 if num == 0.0 else math.inf
+        return num / den
+    keep = [True] * hw + [False] * ((frames - 1) * hw)
+    for loc in range(hw):
+        last = 0
+        for f in range(1, frames):
+            cur = x[f * hw + loc]
+            s = change(cur, x[(f - 1) * hw + loc])
+            lt = change(cur, x[last * hw + loc])
+            k = not (s < tau_short and lt < tau_long)
+            keep[f * hw + loc] = k
+            if k:
+                last = f
+    return keep
+
+
+def restore(buf, mask, frames, hw):
+    """Pruned token (f, loc) takes the value of the nearest earlier kept frame at loc."""
+    out = [list(r) for r in buf]
+    for loc in range(hw):
+        for f in range(1, frames):
+            t = f * hw + loc
+            if not mask[t]:
+                src = f - 1
+                while src > 0 and not mask[src * hw + loc]:
+                    src -= 1
+                out[t] = list(buf[src * hw + loc])  # a kept frame, or frame 0
     return out

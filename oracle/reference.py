@@ -291,3 +291,126 @@ def lipar_step(x, eps, w_qkv, heads: int, hw: int, k: int, sigma: float,
         scatter(out, idx, o_a)
     res.update(q=q, k=pa["k"], v=pa["v"], o_a=o_a)
     return res
+
+
+# ------------------------------------------- f1: cached Euler update, phase window
+
+def round_f32(x) -> np.ndarray:
+    """Round float64 values to the nearest float32, ties to even (storage rounding of an
+    fp32 state)."""
+    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def euler_update(x, v_hat, dt: float, store: str = "f32") -> np.ndarray:
+    """HSA page §2.3: every token, active or skipped, advances by the same Euler increment
+    dt = sigma_{i+1} - sigma_i along its cached velocity v_hat (the velocity of its most
+    recent active step).  One elementwise operation over all N tokens; the exact result is
+    stored in the state's precision: 'f32' or 'bf16' (nearest even) or 'f64' (kept exact,
+    for checks).
+    """
+    y = np.asarray(x, dtype=np.float64) + float(dt) * np.asarray(v_hat, dtype=np.float64)
+    if store == "f32":
+        return round_f32(y)
+    if store == "bf16":
+        return round_bf16(y)
+    if store == "f64":
+        return y
+    raise ValueError(f"unknown store {store!r}")
+
+
+def step_is_dense(step: int, steps: int, window: int) -> bool:
+    """HSA page §2.4: the first and the last ``window`` of the ``steps`` global steps run
+    full, uncached passes for every token; caching is confined to the middle."""
+    return step < window or step >= steps - window
+
+
+def euler_dt(sigmas, step: int) -> float:
+    """sigma_{i+1} - sigma_i, handed to the update as an fp32 value."""
+    return float(np.float32(float(sigmas[step + 1]) - float(sigmas[step])))
+
+
+def hsa_run(x0, w_qkv, heads: int, periods, sigmas, window: int, store: str = "f32") -> list:
+    """HSA page §2.1-§2.4: the sampling loop around the pruned layer.
+
+    T = len(sigmas) - 1 global steps.  At step i the active set is every token when i
+    lies in the phase window (step_is_dense), else the tokens whose period p divides i
+    (schedule_mask).  The layer step (layer_step: projection of the active tokens, KV
+    cache sync, attention over the whole cache, scatter) refreshes the velocity cache
+    v_hat at the active rows -- the layer output stands for the velocity prediction --
+    and then every token advances: x <- euler_update(x, v_hat, sigma_{i+1} - sigma_i).
+    The cache, v_hat and x start at zero, x0 and zero; the state x is stored as
+    ``store``.  Returns one record per step: active indices, v_hat and x after it.
+    """
+    steps = len(sigmas) - 1
+    x = np.array(x0, dtype=np.float64)
+    n, d = x.shape
+    k_cache = np.zeros((n, d))
+    v_cache = np.zeros((n, d))
+    v_hat = np.zeros((n, d))
+    periods = np.asarray(periods)
+    hist = []
+    for i in range(steps):
+        if step_is_dense(i, steps, window):
+            mask = np.ones(n, dtype=bool)
+        else:
+            mask = schedule_mask(periods, i)
+        res = layer_step(x, w_qkv, heads, k_cache, v_cache, v_hat, mask=mask)
+        x = euler_update(x, v_hat, euler_dt(sigmas, i), store)
+        hist.append({"idx": res["idx"], "v_hat": v_hat.copy(), "x": x.copy()})
+    return hist
+
+
+# ------------------------------ f2: long/short-term pruning mask, restoration
+
+def _l1_change(a, b, relative: bool) -> np.ndarray:
+    num = np.abs(a - b).sum(axis=-1)
+    if not relative:
+        return num
+    den = np.abs(b).sum(axis=-1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        s = num / den
+    s = np.where(den == 0.0, np.where(num == 0.0, 0.0, np.inf), s)
+    return s
+
+
+def lif_mask(x, frames: int, hw: int, tau_short: float, tau_long: float,
+             relative: bool = False) -> dict:
+    """LIPAR page §2.B (detection and its improvement): a latent token is compared with the
+    same spatial location in the previous frame (short-term change) and in the most recent
+    frame where that location was kept (long-term change, so that slow drift that stays
+    under the per-frame threshold still forces a refresh).  It is pruned only when both
+    changes are below their thresholds (strictly); frame 0 is always kept.  Changes are L1
+    norms of the row difference (``relative``: divided by the reference row's L1 norm).
+    Frames are processed in order, since the long-term reference depends on the earlier
+    decisions.  Returns the mask (True = kept) and both change scores (+inf on frame 0).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[1]
+    xf = x.reshape(frames, hw, d)
+    keep = np.zeros((frames, hw), dtype=bool)
+    short = np.full((frames, hw), np.inf)
+    long_ = np.full((frames, hw), np.inf)
+    keep[0] = True
+    last = np.zeros(hw, dtype=np.int64)  # frame of the last kept token at each location
+    loc = np.arange(hw)
+    for f in range(1, frames):
+        short[f] = _l1_change(xf[f], xf[f - 1], relative)
+        long_[f] = _l1_change(xf[f], xf[last, loc], relative)
+        keep[f] = ~((short[f] < tau_short) & (long_[f] < tau_long))
+        last = np.where(keep[f], f, last)
+    return {"mask": keep.reshape(-1), "short": short.reshape(-1), "long": long_.reshape(-1)}
+
+
+def restore_frames(buf, mask, frames: int, hw: int) -> np.ndarray:
+    """Dutch LIPAR page §2.D (restoration): after denoising, every pruned token is filled in
+    by duplicating the same location of the previous frame, so the decoder receives the
+    full token sequence.  Along the frame axis this carries the most recent kept token
+    forward.  Kept rows are unchanged; a pruned row in frame 0 (no previous frame) is left
+    as it is.
+    """
+    b = np.array(buf, dtype=np.float64).reshape(frames, hw, -1)
+    m = np.asarray(mask, dtype=bool).reshape(frames, hw)
+    for f in range(1, frames):
+        pruned = ~m[f]
+        b[f, pruned] = b[f - 1, pruned]
+    return b.reshape(frames * hw, -1)

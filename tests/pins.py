@@ -209,3 +209,129 @@ def check_attention(attention):
     qs, ks, vs = q[:5], k[:9], v[:9]
     assert np.allclose(attention(qs, ks, vs, heads), brute.attention(qs.tolist(), ks.tolist(), vs.tolist(), heads),
                        rtol=1e-12, atol=1e-13)
+
+
+# ------------------------------------------------------ f1: cached Euler update
+
+def check_euler(euler_update):
+    r = rng(11)
+    x = r.standard_normal((7, 24)).astype(np.float32).astype(np.float64)
+    v = bf16_values(r.standard_normal((7, 24)))
+    # no step or no velocity: the state is unchanged, bit for bit
+    assert np.array_equal(euler_update(x, v, 0.0), x)
+    assert np.array_equal(euler_update(x, np.zeros_like(v), -0.125), x)
+    # from zero, a power-of-two step scales the velocity exactly
+    assert np.array_equal(euler_update(np.zeros_like(x), v, 0.5), 0.5 * v)
+    # dt = +-1 reduces to one float32 addition / subtraction (numpy's float32 arithmetic)
+    x32, v32 = x.astype(np.float32), v.astype(np.float32)
+    assert np.array_equal(euler_update(x, v, 1.0), (x32 + v32).astype(np.float64))
+    assert np.array_equal(euler_update(x, v, -1.0), (x32 - v32).astype(np.float64))
+    # a general step: the exact value rounded once (pure-Python brute force)
+    dt = float(np.float32(-0.1234567))
+    assert np.array_equal(euler_update(x, v, dt), np.array(brute.euler(x.tolist(), v.tolist(), dt)))
+    # kept exact ('f64'): x + dt * v
+    assert np.array_equal(euler_update(x, v, dt, store="f64"), x + dt * v)
+
+
+def check_window(step_is_dense):
+    assert [step_is_dense(i, 8, 2) for i in range(8)] == [True, True] + [False] * 4 + [True, True]
+    assert not any(step_is_dense(i, 8, 0) for i in range(8))
+    assert all(step_is_dense(i, 8, 4) for i in range(8))
+    assert [step_is_dense(i, 5, 1) for i in range(5)] == [True, False, False, False, True]
+
+
+def _hsa_tiny(seed=12, n=20, dim=16, heads=2):
+    r = rng(seed)
+    x0 = r.standard_normal((n, dim)).astype(np.float32).astype(np.float64)
+    w = bf16_values(r.standard_normal((3 * dim, dim)) / np.sqrt(dim))
+    periods = r.choice([1, 2, 4], size=n)
+    sigmas = [float(np.cos(np.pi * i / 16)) for i in range(9)]  # unequal steps
+    return x0, w, heads, periods, sigmas
+
+
+def check_hsa_run(hsa_run, schedule_mask):
+    x0, w, heads, periods, sigmas = _hsa_tiny()
+    steps = len(sigmas) - 1
+    window = 2
+    hist = hsa_run(x0, w, heads, periods, sigmas, window)
+    bh = brute.hsa_run(x0.tolist(), w.tolist(), heads, periods.tolist(), sigmas, window)
+    for i, (a, b) in enumerate(zip(hist, bh)):
+        assert list(a["idx"]) == b["idx"], i
+        assert np.allclose(a["v_hat"], np.array(b["v_hat"]), rtol=1e-12, atol=1e-12), i
+        # float32 states: equal up to a rounding flip caused by last-bit differences of v_hat
+        assert np.allclose(a["x"], np.array(b["x"]), rtol=2.0 ** -23, atol=1e-12), i
+    n = x0.shape[0]
+    prev = None
+    for i, h in enumerate(hist):
+        # active set: everyone in the window, the period schedule in between
+        want = np.arange(n) if i < window or i >= steps - window else np.flatnonzero(schedule_mask(periods, i))
+        assert np.array_equal(h["idx"], want), i
+        # skipped tokens keep the velocity of their last active step, bit for bit
+        if prev is not None:
+            skipped = np.setdiff1d(np.arange(n), h["idx"])
+            assert np.array_equal(h["v_hat"][skipped], prev["v_hat"][skipped]), i
+        prev = h
+    # exact state: the displacement telescopes to sum_i (sigma_{i+1} - sigma_i) v_hat_i
+    hx = hsa_run(x0, w, heads, periods, sigmas, window, store="f64")
+    disp = sum(float(np.float32(sigmas[i + 1] - sigmas[i])) * hx[i]["v_hat"] for i in range(steps))
+    assert np.allclose(hx[-1]["x"] - x0, disp, rtol=0, atol=1e-12)
+    # a window covering every step makes every step dense
+    assert all(h["idx"].size == n for h in hsa_run(x0, w, heads, periods, sigmas, steps // 2))
+
+
+# ------------------------------- f2: long/short-term pruning mask, restoration
+
+def _drift_clip(frames=10, hw=3, d=8):
+    """Location 0 static, location 1 drifting by a fixed exact step per frame, location 2 random."""
+    r = rng(13)
+    base = bf16_values(r.standard_normal((hw, d)))
+    step = np.full(d, 2.0 ** -6)
+    x = np.zeros((frames, hw, d))
+    for f in range(frames):
+        x[f, 0] = base[0]
+        x[f, 1] = base[1] + f * step
+        x[f, 2] = bf16_values(r.standard_normal(d))
+    return x.reshape(frames * hw, d), float(np.abs(step).sum())
+
+
+def check_lif_mask(lif_mask, token_scores, select_threshold):
+    frames, hw = 10, 3
+    x, c = _drift_clip(frames, hw)
+    # strict comparison: thresholds of 0 keep everything; infinite thresholds keep frame 0 only
+    assert lif_mask(x, frames, hw, 0.0, 0.0)["mask"].all()
+    m = lif_mask(x, frames, hw, np.inf, np.inf)["mask"].reshape(frames, hw)
+    assert m[0].all() and not m[1:].any()
+    # slow drift below the per-frame threshold: the long-term change forces a refresh every
+    # ceil(tau_long / c) frames; the static location is never refreshed
+    res = lif_mask(x, frames, hw, 1.5 * c, 2.5 * c)
+    m = res["mask"].reshape(frames, hw)
+    assert list(np.flatnonzero(m[:, 1])) == [0, 3, 6, 9]
+    assert list(np.flatnonzero(m[:, 0])) == [0]
+    assert np.allclose(res["short"].reshape(frames, hw)[1:, 1], c, rtol=0, atol=0)
+    assert list(res["long"].reshape(frames, hw)[1:4, 1]) == [c, 2 * c, 3 * c]
+    # without a long-term limit it is the plain threshold rule on the previous-frame change
+    r = rng(14)
+    y = bf16_values(r.standard_normal((6 * 5, 12)))
+    s = token_scores(y, None, 5, relative=False)
+    tau = float(np.median(s[5:]))
+    assert np.array_equal(lif_mask(y, 6, 5, tau, np.inf)["mask"], select_threshold(s, tau))
+    # brute force, absolute and relative changes
+    for rel in (False, True):
+        tau_s = float(np.quantile(token_scores(y, None, 5, relative=rel)[5:], 0.6))
+        got = lif_mask(y, 6, 5, tau_s, 1.7 * tau_s, relative=rel)["mask"]
+        assert list(got) == brute.lif_mask(y.tolist(), 6, 5, tau_s, 1.7 * tau_s, relative=rel)
+
+
+def check_restore(restore_frames):
+    r = rng(15)
+    frames, hw, d = 6, 4, 8
+    buf = bf16_values(r.standard_normal((frames * hw, d)))
+    assert np.array_equal(restore_frames(buf, np.ones(frames * hw, bool), frames, hw), buf)
+    only0 = np.zeros(frames * hw, bool)
+    only0[:hw] = True
+    assert np.array_equal(restore_frames(buf, only0, frames, hw), np.tile(buf[:hw], (frames, 1)))
+    mask = r.random(frames * hw) < 0.5
+    mask[:hw] = True
+    got = restore_frames(buf, mask, frames, hw)
+    assert np.array_equal(got[mask], buf[mask])
+    assert np.array_equal(got, np.array(brute.restore(buf.tolist(), mask.tolist(), frames, hw)))

@@ -226,3 +226,25 @@ def test_oracle_on_tiny_workload_is_consistent():
     static = inp["static"].numpy()
     assert res["idx"].size == 64 and not static[res["idx"]].any()
     assert np.isfinite(out).all()
+
+
+# ------------------------------------------------ f1 / f2 (steps beside the layer)
+
+def test_euler_pinned():
+    pins.check_euler(ref.euler_update)
+
+
+def test_phase_window_pinned():
+    pins.check_window(ref.step_is_dense)
+
+
+def test_hsa_run_pinned():
+    pins.check_hsa_run(ref.hsa_run, ref.schedule_mask)
+
+
+def test_lif_mask_pinned():
+    pins.check_lif_mask(ref.lif_mask, ref.token_scores, ref.select_threshold)
+
+
+def test_restore_pinned():
+    pins.check_restore(ref.restore_frames)

@@ -159,3 +159,91 @@ def _attn_no_max_shift_lse(q, k, v, heads, scale=None, block=256, return_lse=Fal
 @pytest.mark.parametrize("bad", [_attn_no_scale, _attn_head0_keys, _attn_softmax_wrong_axis, _attn_no_max_shift_lse])
 def test_attention_mutations_caught(bad):
     _fails(pins.check_attention, bad)
+
+
+# ------------------------------------------------ f1: Euler update and loop
+
+def _euler_wrong_sign(x, v_hat, dt, store="f32"):
+    return ref.euler_update(x, v_hat, -dt, store)
+
+
+def _euler_no_rounding(x, v_hat, dt, store="f32"):
+    return ref.euler_update(x, v_hat, dt, "f64")
+
+
+@pytest.mark.parametrize("bad", [_euler_wrong_sign, _euler_no_rounding])
+def test_euler_mutations_caught(bad):
+    _fails(pins.check_euler, bad)
+
+
+def test_window_off_by_one_caught():
+    _fails(pins.check_window, lambda i, steps, window: i <= window or i >= steps - window)
+
+
+def _hsa_with(**patch):
+    """hsa_run with one of its steps replaced (a planted mistake)."""
+    def run(x0, w, heads, periods, sigmas, window, store="f32"):
+        saved = {k: getattr(ref, k) for k in patch}
+        try:
+            for k, f in patch.items():
+                setattr(ref, k, f)
+            return ref.hsa_run(x0, w, heads, periods, sigmas, window, store)
+        finally:
+            for k, f in saved.items():
+                setattr(ref, k, f)
+    return run
+
+
+def _dt_previous_interval(sigmas, step):
+    return float(np.float32(float(sigmas[max(step, 1)]) - float(sigmas[max(step, 1) - 1])))
+
+
+def _layer_step_forgets_velocity(x_cur, w_qkv, heads, k_cache, v_cache, out, **kw):
+    out[:] = 0.0  # skipped tokens lose their cached velocity
+    return _orig_layer_step(x_cur, w_qkv, heads, k_cache, v_cache, out, **kw)
+
+
+_orig_layer_step = ref.layer_step
+
+
+@pytest.mark.parametrize("patch", [
+    {"euler_dt": _dt_previous_interval},
+    {"layer_step": _layer_step_forgets_velocity},
+    {"step_is_dense": lambda i, steps, window: i < window},
+])
+def test_hsa_run_mutations_caught(patch):
+    _fails(pins.check_hsa_run, _hsa_with(**patch), ref.schedule_mask)
+
+
+# ----------------------------------- f2: long/short-term mask, restoration
+
+def _lif_previous_frame_only(x, frames, hw, tau_short, tau_long, relative=False):
+    """long-term reference taken as the previous frame (no tracking of the last kept frame)"""
+    s = ref.token_scores(x, None, hw, relative=relative)
+    keep = ~((s < tau_short) & (s < tau_long))
+    keep[:hw] = True
+    return {"mask": keep, "short": s, "long": s}
+
+
+def _lif_not_strict(x, frames, hw, tau_short, tau_long, relative=False):
+    return ref.lif_mask(x, frames, hw, np.nextafter(tau_short, np.inf), np.nextafter(tau_long, np.inf),
+                        relative)
+
+
+@pytest.mark.parametrize("bad", [_lif_previous_frame_only, _lif_not_strict])
+def test_lif_mask_mutations_caught(bad):
+    _fails(pins.check_lif_mask, bad, ref.token_scores, ref.select_threshold)
+
+
+def _restore_from_original(buf, mask, frames, hw):
+    """copies the previous frame's original row instead of its restored value"""
+    b = np.array(buf, dtype=np.float64).reshape(frames, hw, -1)
+    src = b.copy()
+    m = np.asarray(mask, bool).reshape(frames, hw)
+    for f in range(1, frames):
+        b[f, ~m[f]] = src[f - 1, ~m[f]]
+    return b.reshape(frames * hw, -1)
+
+
+def test_restore_mutation_caught():
+    _fails(pins.check_restore, _restore_from_original)
