@@ -259,7 +259,7 @@ def layer_step(x_cur, w_qkv, heads: int, k_cache, v_cache, out, *, mask=None, x_
 
 
 def lipar_step(x, eps, w_qkv, heads: int, hw: int, k: int, sigma: float,
-               k_cache, v_cache, out, query_rows=None) -> dict:
+               k_cache, v_cache, out, query_rows=None, mask=None) -> dict:
     """One inter-frame pruned pass over a whole clip (LIPAR page §2.B and §2.C).
 
     Tokens are scored against the same location one frame earlier (offset
@@ -269,10 +269,11 @@ def lipar_step(x, eps, w_qkv, heads: int, hw: int, k: int, sigma: float,
     rewritten; active queries attend over the whole cache.
 
     ``query_rows`` (positions into the active list) restricts the attention to a
-    sample of active queries; rows are independent given the cache.
+    sample of active queries; rows are independent given the cache.  A given
+    ``mask`` (e.g. lif_mask's long/short-term mask) replaces the top-k choice.
     """
     scores = token_scores(x, None, hw)
-    mask = select_topk(scores, k)
+    mask = select_topk(scores, k) if mask is None else np.asarray(mask, dtype=bool)
     idx, pidx = compact(mask)
     res = {"scores": scores, "mask": mask, "idx": idx, "pidx": pidx}
     xa = np.asarray(x, dtype=np.float64)[idx]
@@ -304,15 +305,17 @@ def round_f32(x) -> np.ndarray:
 def euler_update(x, v_hat, dt: float, store: str = "f32") -> np.ndarray:
     """HSA page §2.3: every token, active or skipped, advances by the same Euler increment
     dt = sigma_{i+1} - sigma_i along its cached velocity v_hat (the velocity of its most
-    recent active step).  One elementwise operation over all N tokens; the exact result is
-    stored in the state's precision: 'f32' or 'bf16' (nearest even) or 'f64' (kept exact,
-    for checks).
+    recent active step).  One elementwise operation over all N tokens.
+
+    Precision points (the page fixes none): the update is one fp32 operation, so the exact
+    x + dt * v_hat is rounded once to fp32; a bf16 state then stores that fp32 value rounded
+    to nearest even.  store: 'f32', 'bf16', or 'f64' (kept exact, for checks).
     """
     y = np.asarray(x, dtype=np.float64) + float(dt) * np.asarray(v_hat, dtype=np.float64)
     if store == "f32":
         return round_f32(y)
     if store == "bf16":
-        return round_bf16(y)
+        return round_bf16(round_f32(y))
     if store == "f64":
         return y
     raise ValueError(f"unknown store {store!r}")

@@ -231,6 +231,11 @@ def check_euler(euler_update):
     assert np.array_equal(euler_update(x, v, dt), np.array(brute.euler(x.tolist(), v.tolist(), dt)))
     # kept exact ('f64'): x + dt * v
     assert np.array_equal(euler_update(x, v, dt, store="f64"), x + dt * v)
+    # a bf16 state stores the fp32 result rounded to bf16 (torch's float32 -> bfloat16)
+    xb = bf16_values(x)
+    f32res = euler_update(xb, v, dt)
+    want = torch.from_numpy(f32res.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(euler_update(xb, v, dt, store="bf16"), want)
 
 
 def check_window(step_is_dense):
