@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define TSA_ABI_VERSION 2
+#define TSA_ABI_VERSION 3
 
 typedef uint16_t tsa_bf16;
 
@@ -241,6 +241,57 @@ tsa_status tsa_scatter_out(const tsa_bf16* o_a, const int32_t* rows, int64_t n, 
 tsa_status tsa_gather_rows(const tsa_bf16* x, int64_t n_x_rows, const int32_t* rows, int64_t n,
                            int64_t dim, const tsa_bf16* eps, int64_t src_row_offset, float sigma,
                            tsa_bf16* dst, void* stream);
+
+/*
+ * [HSA] §2.3 cached Euler update: after a global step every token, active or
+ * skipped, advances by the same increment dt = sigma_{i+1} - sigma_i along
+ * its cached velocity (the velocity of its most recent active step):
+ *   x[r, j] <- x[r, j] + dt * v_hat[r, j]   for all n_rows rows,
+ * computed as one fused multiply-add in fp32 (TSA_F32 state: rounded once;
+ * TSA_BF16 state: that result rounded to nearest even).
+ *   x       device [n_rows, dim] of x_dtype, updated in place.
+ *   v_hat   device bf16 [n_rows, dim] (e.g. the layer output in token order,
+ *           whose skipped rows keep their last active value).
+ * dim must be a multiple of 8; dt finite.  Errors: INVALID_ARG, SHAPE, DTYPE,
+ * ALIGNMENT, HIP.
+ */
+tsa_status tsa_euler_update(void* x, int x_dtype, const tsa_bf16* v_hat, int64_t n_rows, int64_t dim,
+                            float dt, void* stream);
+
+/*
+ * [LIPAR] §2.B pruning mask with short- and long-term changes.  Tokens are
+ * frame-major, token t = f * hw + l for frame f and spatial location l.  For
+ * f >= 1 the short-term change compares row t with the same location in
+ * frame f-1, the long-term change with the same location in the most recent
+ * earlier frame where that location was kept; changes are L1 norms of the
+ * row difference (TSA_SCORE_REL_L1: divided by the L1 norm of the reference
+ * row, 0/0 -> 0, x/0 -> +inf).  Token t is pruned (mask 0) iff
+ * short < tau_short and long < tau_long; frame 0 is always kept (mask 1,
+ * scores +inf).  Sums in fp32, fixed order.
+ *   x          device [frames * hw, dim] of dtype (TSA_F32 or TSA_BF16).
+ *   mask_out   device u8[frames * hw].
+ *   short_out, long_out  device f32[frames * hw] or NULL.
+ * dim must be a multiple of 8, at most 8192 (bf16) or 4096 (fp32); the
+ * thresholds must not be NaN (+inf allowed).  The mask feeds
+ * tsa_select_active in TSA_SELECT_MASK mode.
+ * Errors: INVALID_ARG, SHAPE, DTYPE, ALIGNMENT, HIP.
+ */
+tsa_status tsa_lif_mask(const void* x, int dtype, int64_t frames, int64_t hw, int64_t dim, int score_kind,
+                        float tau_short, float tau_long, uint8_t* mask_out, float* short_out,
+                        float* long_out, void* stream);
+
+/*
+ * [LIPAR] (Dutch page) §2.D restoration: after denoising, every pruned token
+ * (mask 0) is filled in with the same location of the previous frame, so the
+ * result is a full token sequence; along the frame axis this carries the most
+ * recent kept row forward.  Kept rows and frame-0 rows are not written.
+ *   buf    device [frames * hw, dim] of dtype, frame-major as in tsa_lif_mask,
+ *          updated in place.
+ *   mask   device u8[frames * hw].
+ * dim must be a multiple of 8.  Errors: INVALID_ARG, SHAPE, DTYPE, ALIGNMENT, HIP.
+ */
+tsa_status tsa_restore_frames(void* buf, int dtype, const uint8_t* mask, int64_t frames, int64_t hw,
+                              int64_t dim, void* stream);
 
 #ifdef __cplusplus
 }

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(root):
 
 
 def test_version_and_status_strings():
-    assert tsa.abi_version() == 2
+    assert tsa.abi_version() == 3
     assert tsa.status_string(0) == "ok"
     assert "shape" in tsa.status_string(B.ERR_SHAPE)
     assert tsa.status_string(99) == "unknown status"

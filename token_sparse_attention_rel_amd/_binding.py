@@ -44,6 +44,9 @@ _SIGNATURES = {
     "tsa_attention_workspace_bytes": (_size, [_i64, _i64, _int, _int]),
     "tsa_scatter_out": (_int, [_vp, _vp, _i64, _vp, _i64, _i64, _vp]),
     "tsa_gather_rows": (_int, [_vp, _i64, _vp, _i64, _i64, _vp, _i64, _f32, _vp, _vp]),
+    "tsa_euler_update": (_int, [_vp, _int, _vp, _i64, _i64, _f32, _vp]),
+    "tsa_lif_mask": (_int, [_vp, _int, _i64, _i64, _i64, _int, _f32, _f32, _vp, _vp, _vp, _vp]),
+    "tsa_restore_frames": (_int, [_vp, _int, _vp, _i64, _i64, _i64, _vp]),
 }
 
 _lib_handle = None
@@ -211,3 +214,26 @@ def gather_rows(x, rows, n, dst, *, eps=None, src_row_offset=0, sigma=0.0, strea
                                _ptr(eps), int(src_row_offset), float(sigma), _ptr(dst),
                                _stream(stream))
     _check("tsa_gather_rows", st)
+
+
+def euler_update(x, v_hat, dt, stream=None):
+    """Cached Euler update x <- x + dt * v_hat over all rows (tsa_euler_update)."""
+    st = lib().tsa_euler_update(_ptr(x), _dtype_code(x), _ptr(v_hat), int(x.shape[0]), int(x.shape[1]),
+                                float(dt), _stream(stream))
+    _check("tsa_euler_update", st)
+
+
+def lif_mask(x, frames, hw, tau_short, tau_long, mask_out, *, score_kind=SCORE_ABS_L1, short_out=None,
+             long_out=None, stream=None):
+    """Long/short-term inter-frame pruning mask (tsa_lif_mask); x is [frames*hw, dim]."""
+    st = lib().tsa_lif_mask(_ptr(x), _dtype_code(x), int(frames), int(hw), int(x.shape[1]), int(score_kind),
+                            float(tau_short), float(tau_long), _ptr(mask_out), _ptr(short_out),
+                            _ptr(long_out), _stream(stream))
+    _check("tsa_lif_mask", st)
+
+
+def restore_frames(buf, mask, frames, hw, stream=None):
+    """Forward fill of pruned tokens from the previous frame (tsa_restore_frames)."""
+    st = lib().tsa_restore_frames(_ptr(buf), _dtype_code(buf), _ptr(mask), int(frames), int(hw),
+                                  int(buf.shape[1]), _stream(stream))
+    _check("tsa_restore_frames", st)

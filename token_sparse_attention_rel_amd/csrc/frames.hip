@@ -1,0 +1,236 @@
+// Steps beside the pruned layer: the cached Euler update of the sampler, the
+// long/short-term inter-frame pruning mask and the restoration of pruned frames.
+//
+// Euler (HSA page §2.3): after every global step all N tokens advance by the
+// same increment dt = sigma_{i+1} - sigma_i along their cached velocity, one
+// elementwise pass: x <- x + dt * v_hat.  HBM-bound.
+//
+// Pruning mask (LIPAR page §2.B): each latent token is compared with the same
+// spatial location one frame earlier (short-term change) and in the most
+// recent frame where that location was kept (long-term change); it is pruned
+// only when both are below their thresholds.  The long-term reference depends
+// on the decisions of earlier frames, so each location is scanned frame by
+// frame by one workgroup that keeps the previous and the reference row in
+// registers: every latent row is read once.
+//
+// Restoration (Dutch LIPAR page §2.D): after denoising, a pruned token takes
+// the value of the same location in the previous frame -- a forward fill along
+// the frame axis.  One thread per 16-byte slice of a location's row carries
+// the last kept slice down the frames: kept rows are read once, pruned rows
+// written once.
+#include "common.h"
+#include "kernels.h"
+
+namespace tsa {
+
+// ------------------------------------------------------------------ Euler
+
+// x (fp32 or bf16) += dt * v (bf16), 8 elements per thread and iteration.
+// fp32: fmaf rounds the exact value once; bf16: that fp32 result is rounded to
+// nearest even.
+template <typename T>
+__global__ __launch_bounds__(256) void euler_kernel(T* __restrict__ x, const uint16_t* __restrict__ v,
+                                                    long n8, float dt) {
+  for (long c = static_cast<long>(blockIdx.x) * 256 + threadIdx.x; c < n8;
+       c += static_cast<long>(gridDim.x) * 256) {
+    float fv[8];
+    unpack8(reinterpret_cast<const u32x4*>(v)[c], fv);
+    if constexpr (sizeof(T) == 4) {
+      f32x4* xp = reinterpret_cast<f32x4*>(x) + 2 * c;
+      f32x4 a = xp[0], b = xp[1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = fmaf(dt, fv[i], a[i]);
+        b[i] = fmaf(dt, fv[4 + i], b[i]);
+      }
+      xp[0] = a;
+      xp[1] = b;
+    } else {
+      u32x4* xp = reinterpret_cast<u32x4*>(x) + c;
+      float fx[8];
+      unpack8(*xp, fx);
+      u32x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        o[i] = pack_bf16x2(fmaf(dt, fv[2 * i], fx[2 * i]), fmaf(dt, fv[2 * i + 1], fx[2 * i + 1]));
+      *xp = o;
+    }
+  }
+}
+
+hipError_t launch_euler(void* x, int x_dtype, const uint16_t* v, long n_elems, float dt, hipStream_t s) {
+  const long n8 = n_elems / 8;
+  const long blocks = (n8 + 255) / 256;
+  const dim3 grid(static_cast<unsigned>(blocks < 8192 ? blocks : 8192));
+  if (x_dtype == kDtypeF32)
+    hipLaunchKernelGGL(euler_kernel<float>, grid, dim3(256), 0, s, static_cast<float*>(x), v, n8, dt);
+  else
+    hipLaunchKernelGGL(euler_kernel<uint16_t>, grid, dim3(256), 0, s, static_cast<uint16_t*>(x), v, n8, dt);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------- pruning mask
+
+constexpr int kLifThreads = 256;
+
+template <typename T>
+struct Slice;  // one 16-byte slice of a row as fp32
+
+template <>
+struct Slice<uint16_t> {
+  static constexpr int kVec = 8;
+  __device__ static void load(const uint16_t* p, float* f) { unpack8(*reinterpret_cast<const u32x4*>(p), f); }
+};
+
+template <>
+struct Slice<float> {
+  static constexpr int kVec = 4;
+  __device__ static void load(const float* p, float* f) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(p);
+    f[0] = v[0]; f[1] = v[1]; f[2] = v[2]; f[3] = v[3];
+  }
+};
+
+// Sum four values over the workgroup in a fixed order (wave butterflies, then
+// the four wave partials in wave order): deterministic.
+__device__ __forceinline__ void block_sum4(float v[4], float (*part)[4]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = wave_sum(v[i]);
+  if (lane == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) part[wave][i] = v[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = (part[0][i] + part[1][i]) + (part[2][i] + part[3][i]);
+  __syncthreads();  // part is rewritten by the next call
+}
+
+__device__ __forceinline__ float l1_score(float num, float den, int relative) {
+  if (!relative) return num;
+  if (den == 0.f) return num == 0.f ? 0.f : __builtin_inff();
+  return num / den;
+}
+
+// One workgroup per spatial location; CPT 16-byte slices per thread and row.
+template <typename T, int CPT>
+__global__ __launch_bounds__(kLifThreads) void lif_mask_kernel(const T* __restrict__ x, long frames, long hw,
+                                                               long dim, int relative, float tau_s,
+                                                               float tau_l, uint8_t* __restrict__ mask,
+                                                               float* __restrict__ short_out,
+                                                               float* __restrict__ long_out) {
+  constexpr int V = Slice<T>::kVec;
+  __shared__ float part[kLifThreads / 64][4];
+  const long loc = blockIdx.x;
+  const long n_sl = dim / V;
+  float prev[CPT][V], ref[CPT][V], cur[CPT][V];
+  auto load_row = [&](float (*dst)[V], long f) {
+    const T* row = x + (f * hw + loc) * dim;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const long sl = threadIdx.x + static_cast<long>(kLifThreads) * j;
+      if (sl < n_sl) {
+        Slice<T>::load(row + sl * V, dst[j]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < V; ++e) dst[j][e] = 0.f;
+      }
+    }
+  };
+  load_row(prev, 0);
+#pragma unroll
+  for (int j = 0; j < CPT; ++j)
+#pragma unroll
+    for (int e = 0; e < V; ++e) ref[j][e] = prev[j][e];
+  if (threadIdx.x == 0) {
+    mask[loc] = 1;
+    if (short_out) short_out[loc] = __builtin_inff();
+    if (long_out) long_out[loc] = __builtin_inff();
+  }
+  for (long f = 1; f < frames; ++f) {
+    load_row(cur, f);
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};  // short num, short den, long num, long den
+#pragma unroll
+    for (int j = 0; j < CPT; ++j)
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        acc[0] += fabsf(cur[j][e] - prev[j][e]);
+        acc[1] += fabsf(prev[j][e]);
+        acc[2] += fabsf(cur[j][e] - ref[j][e]);
+        acc[3] += fabsf(ref[j][e]);
+      }
+    block_sum4(acc, part);
+    const float ss = l1_score(acc[0], acc[1], relative);
+    const float ls = l1_score(acc[2], acc[3], relative);
+    const bool keep = !((ss < tau_s) && (ls < tau_l));
+    const long t = f * hw + loc;
+    if (threadIdx.x == 0) {
+      mask[t] = keep ? 1 : 0;
+      if (short_out) short_out[t] = ss;
+      if (long_out) long_out[t] = ls;
+    }
+#pragma unroll
+    for (int j = 0; j < CPT; ++j)
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        if (keep) ref[j][e] = cur[j][e];
+        prev[j][e] = cur[j][e];
+      }
+  }
+}
+
+template <typename T>
+hipError_t launch_lif_t(const T* x, long frames, long hw, long dim, int relative, float tau_s, float tau_l,
+                        uint8_t* mask, float* so, float* lo, hipStream_t s) {
+  const long cpt = (dim / Slice<T>::kVec + kLifThreads - 1) / kLifThreads;
+  const dim3 grid(static_cast<unsigned>(hw)), block(kLifThreads);
+  switch (cpt) {
+    case 1: hipLaunchKernelGGL((lif_mask_kernel<T, 1>), grid, block, 0, s, x, frames, hw, dim, relative, tau_s, tau_l, mask, so, lo); break;
+    case 2: hipLaunchKernelGGL((lif_mask_kernel<T, 2>), grid, block, 0, s, x, frames, hw, dim, relative, tau_s, tau_l, mask, so, lo); break;
+    case 3: hipLaunchKernelGGL((lif_mask_kernel<T, 3>), grid, block, 0, s, x, frames, hw, dim, relative, tau_s, tau_l, mask, so, lo); break;
+    case 4: hipLaunchKernelGGL((lif_mask_kernel<T, 4>), grid, block, 0, s, x, frames, hw, dim, relative, tau_s, tau_l, mask, so, lo); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+long lif_max_dim(int dtype) { return (dtype == kDtypeF32 ? 4L : 8L) * kLifThreads * 4; }
+
+hipError_t launch_lif_mask(const void* x, int dtype, long frames, long hw, long dim, int relative, float tau_s,
+                           float tau_l, uint8_t* mask, float* short_out, float* long_out, hipStream_t s) {
+  if (dtype == kDtypeF32)
+    return launch_lif_t(static_cast<const float*>(x), frames, hw, dim, relative, tau_s, tau_l, mask, short_out,
+                        long_out, s);
+  return launch_lif_t(static_cast<const uint16_t*>(x), frames, hw, dim, relative, tau_s, tau_l, mask, short_out,
+                      long_out, s);
+}
+
+// ----------------------------------------------------------- restoration
+
+// Thread = (location, 16-byte slice); rows of row_bytes bytes.
+__global__ __launch_bounds__(256) void restore_kernel(u32x4* __restrict__ buf, const uint8_t* __restrict__ mask,
+                                                      long frames, long hw, long slices) {
+  const long id = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
+  if (id >= hw * slices) return;
+  const long loc = id / slices, sl = id - loc * slices;
+  u32x4 carry = buf[loc * slices + sl];
+  for (long f = 1; f < frames; ++f) {
+    const long t = f * hw + loc;
+    u32x4* p = buf + t * slices + sl;
+    if (mask[t])
+      carry = *p;
+    else
+      *p = carry;
+  }
+}
+
+hipError_t launch_restore(void* buf, const uint8_t* mask, long frames, long hw, long row_bytes, hipStream_t s) {
+  const long slices = row_bytes / 16;
+  const long threads = hw * slices;
+  hipLaunchKernelGGL(restore_kernel, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, s,
+                     static_cast<u32x4*>(buf), mask, frames, hw, slices);
+  return hipGetLastError();
+}
+
+}  // namespace tsa

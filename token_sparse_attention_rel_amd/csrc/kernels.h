@@ -58,4 +58,11 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t
                             const int* out_rows, float* lse, void* ws, size_t ws_bytes,
                             hipStream_t s);
 
+// frames.hip
+hipError_t launch_euler(void* x, int x_dtype, const uint16_t* v, long n_elems, float dt, hipStream_t s);
+long lif_max_dim(int dtype);
+hipError_t launch_lif_mask(const void* x, int dtype, long frames, long hw, long dim, int relative, float tau_s,
+                           float tau_l, uint8_t* mask, float* short_out, float* long_out, hipStream_t s);
+hipError_t launch_restore(void* buf, const uint8_t* mask, long frames, long hw, long row_bytes, hipStream_t s);
+
 }  // namespace tsa

@@ -220,4 +220,43 @@ tsa_status tsa_gather_rows(const tsa_bf16* x, int64_t n_x_rows, const int32_t* r
   return from_hip(tsa::launch_gather_rows(src, n, dim, dst, as_stream(stream)));
 }
 
+tsa_status tsa_euler_update(void* x, int x_dtype, const tsa_bf16* v_hat, int64_t n_rows, int64_t dim,
+                            float dt, void* stream) {
+  if (!x || !v_hat || isnan(dt) || isinf(dt)) return TSA_ERR_INVALID_ARG;
+  if (x_dtype != TSA_F32 && x_dtype != TSA_BF16) return TSA_ERR_DTYPE;
+  if (n_rows < 0 || n_rows > kMaxRows || dim <= 0 || dim % 8 != 0 || dim > kMaxRows) return TSA_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(v_hat)) return TSA_ERR_ALIGNMENT;
+  if (n_rows == 0) return TSA_OK;
+  return from_hip(tsa::launch_euler(x, x_dtype, v_hat, n_rows * dim, dt, as_stream(stream)));
+}
+
+tsa_status tsa_lif_mask(const void* x, int dtype, int64_t frames, int64_t hw, int64_t dim, int score_kind,
+                        float tau_short, float tau_long, uint8_t* mask_out, float* short_out,
+                        float* long_out, void* stream) {
+  if (!x || !mask_out || isnan(tau_short) || isnan(tau_long)) return TSA_ERR_INVALID_ARG;
+  if (score_kind != TSA_SCORE_REL_L1 && score_kind != TSA_SCORE_ABS_L1) return TSA_ERR_INVALID_ARG;
+  if (dtype != TSA_F32 && dtype != TSA_BF16) return TSA_ERR_DTYPE;
+  if (frames < 1 || hw < 1 || frames > kMaxRows || hw > kMaxRows || frames * hw > kMaxRows)
+    return TSA_ERR_SHAPE;
+  if (dim <= 0 || dim % 8 != 0 || dim > tsa::lif_max_dim(dtype)) return TSA_ERR_SHAPE;
+  if (!aligned16(x) || (short_out && !aligned4(short_out)) || (long_out && !aligned4(long_out)))
+    return TSA_ERR_ALIGNMENT;
+  return from_hip(tsa::launch_lif_mask(x, dtype, frames, hw, dim, score_kind == TSA_SCORE_REL_L1, tau_short,
+                                       tau_long, mask_out, short_out, long_out, as_stream(stream)));
+}
+
+tsa_status tsa_restore_frames(void* buf, int dtype, const uint8_t* mask, int64_t frames, int64_t hw,
+                              int64_t dim, void* stream) {
+  if (!buf || !mask) return TSA_ERR_INVALID_ARG;
+  if (dtype != TSA_F32 && dtype != TSA_BF16) return TSA_ERR_DTYPE;
+  if (frames < 1 || hw < 1 || frames > kMaxRows || hw > kMaxRows || frames * hw > kMaxRows)
+    return TSA_ERR_SHAPE;
+  if (dim <= 0 || dim % 8 != 0 || dim > kMaxRows) return TSA_ERR_SHAPE;
+  const int64_t row_bytes = dim * (dtype == TSA_F32 ? 4 : 2);
+  if (hw * (row_bytes / 16) > kMaxRows * 64) return TSA_ERR_SHAPE;  // grid size
+  if (!aligned16(buf)) return TSA_ERR_ALIGNMENT;
+  if (frames == 1) return TSA_OK;
+  return from_hip(tsa::launch_restore(buf, mask, frames, hw, row_bytes, as_stream(stream)));
+}
+
 }  // extern "C"

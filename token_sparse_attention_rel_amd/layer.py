@@ -40,6 +40,7 @@ class PrunedAttentionLayer:
         self.q_a = torch.empty(n, dim, dtype=bf, device=dev)
         self._k_a = None
         self._v_a = None
+        self._lif_mask = None
         self._o_a = None
         ws = B.select_workspace_bytes(n)
         self.workspace = torch.empty(max(ws, 16) + n, dtype=torch.uint8, device=dev)
@@ -131,6 +132,27 @@ class PrunedAttentionLayer:
         the same location one frame earlier, keep the top k, project active tokens from their
         latent and pruned tokens from the recovered row, attend, scatter."""
         self.select(x, None, k=k, ref_row_offset=hw, stream=stream)
+        self._lipar_forward(x, eps, hw, k, sigma, stream)
+
+    def step_lipar_lif(self, x, eps, frames: int, hw: int, tau_short: float, tau_long: float,
+                       sigma: float, *, score_kind=B.SCORE_ABS_L1, restore=True, stream=None) -> int:
+        """Inter-frame pass with the long/short-term pruning mask (LIPAR page §2.B): a token is
+        pruned when its change against the previous frame and against the last kept frame at
+        its location are both below threshold.  Then the pass of step_lipar on that active
+        set and, with ``restore``, the pruned rows of the output filled in from the previous
+        frame (Dutch LIPAR page §2.D).  Reads the active count back (one synchronisation)."""
+        if self._lif_mask is None:
+            self._lif_mask = torch.empty(self.n, dtype=torch.uint8, device=self.device)
+        B.lif_mask(x, frames, hw, tau_short, tau_long, self._lif_mask, score_kind=score_kind,
+                   stream=stream)
+        self.select(None, mask=self._lif_mask, stream=stream)
+        k = int(self.n_active.item())
+        self._lipar_forward(x, eps, hw, k, sigma, stream)
+        if restore:
+            B.restore_frames(self.out, self._lif_mask, frames, hw, stream=stream)
+        return k
+
+    def _lipar_forward(self, x, eps, hw, k, sigma, stream):
         B.qkv_active(x, self.idx, k, self.w_qkv, q_out=self.q_a, k_out=self.k_cache,
                      v_out=self.v_cache, out_is_cache=True, n_cache=self.n, stream=stream)
         n_p = self.n - k
@@ -142,6 +164,38 @@ class PrunedAttentionLayer:
             B.sparse_query_attention(self.q_a, self.k_cache, self.v_cache, k, self.heads,
                                      self.head_dim, self.out, out_rows=self.idx,
                                      workspace=self.attention_workspace(k), stream=stream)
+
+    # ------------------------------------------------------- sampling loop
+
+    def dense_forward(self, x, stream=None) -> None:
+        """Every token active: QKV of all rows straight into the cache, attention of all
+        queries written in token order (no selection, no index indirection)."""
+        B.qkv_active(x, None, self.n, self.w_qkv, q_out=self.q_a, k_out=self.k_cache,
+                     v_out=self.v_cache, stream=stream)
+        B.sparse_query_attention(self.q_a, self.k_cache, self.v_cache, self.n, self.heads,
+                                 self.head_dim, self.out, workspace=self.attention_workspace(self.n),
+                                 stream=stream)
+
+    def hsa_run(self, x, periods, sigmas, window: int, group_counts, group_periods, *,
+                stream=None, on_step=None) -> None:
+        """HSA page §2.1-§2.4: the sampling loop around the layer, on the state x (fp32 or
+        bf16 [n, dim], updated in place).  Step i is dense inside the phase window (the first
+        and last ``window`` steps), else it runs the tokens whose period divides i; the layer
+        output, whose skipped rows keep their last value, is the cached velocity, and every
+        token then advances by x <- x + (sigma_{i+1} - sigma_i) * v_hat.  ``periods`` is the
+        device u8 period of every token (assign_groups); ``group_counts``/``group_periods``
+        give the per-step active counts on the host, so no step synchronises."""
+        steps = len(sigmas) - 1
+        for i in range(steps):
+            if i < window or i >= steps - window:
+                self.dense_forward(x, stream=stream)
+            else:
+                self.select(None, periods=periods, step=i, stream=stream)
+                self.forward_active(x, hsa_active_count(group_counts, group_periods, i),
+                                    stream=stream)
+            B.euler_update(x, self.out, float(sigmas[i + 1]) - float(sigmas[i]), stream=stream)
+            if on_step is not None:
+                on_step(i)
 
 
 def hsa_active_count(group_counts, group_periods, step: int) -> int:

@@ -15,7 +15,8 @@ from dataclasses import dataclass, field
 @dataclass(frozen=True)
 class Config:
     name: str
-    kind: str  # "step" (one layer step), "hsa" (T-step schedule loop), "lipar" (inter-frame sweep)
+    kind: str  # "step" (one layer step), "hsa" (T-step schedule), "hsa_loop" (sampling loop with
+    # Euler update and phase window), "lipar" (inter-frame sweep), "lipar_lif" (long/short-term mask)
     frames: int
     height: int
     width: int
@@ -32,6 +33,9 @@ class Config:
     group_budgets: tuple = ()  # "hsa": step budget s_k of each group (divides T)
     sigma: float = 0.0  # "lipar": re-noising level of the recovered pruned tokens
     sweep_pcts: tuple = field(default_factory=tuple)  # "lipar": active percentages swept
+    window: int = 0  # "hsa_loop": the first and last `window` steps run dense
+    tau_short: float = 0.0  # "lipar_lif": threshold on the L1 change against the previous frame
+    tau_long: float = 0.0  # "lipar_lif": threshold on the L1 change against the last kept frame
 
     @property
     def n(self) -> int:
@@ -43,7 +47,7 @@ class Config:
 
     @property
     def n_static(self) -> int:
-        if self.kind == "lipar":
+        if self.kind.startswith("lipar"):
             return self.static_pct * self.hw // 100
         return self.static_pct * self.n // 100
 
@@ -59,6 +63,10 @@ class Config:
 
     def sweep_counts(self) -> tuple:
         return tuple(p * self.n // 100 for p in self.sweep_pcts)
+
+    def sigmas(self) -> list:
+        """Noise levels sigma_0..sigma_T of the sampling loop: linear from 1 to 0."""
+        return [1.0 - i / self.steps for i in range(self.steps + 1)]
 
     def attn_flops(self, n_active: int) -> int:
         """Algorithmic attention work of one layer step: 4 * N_a * N * d * H."""
@@ -80,10 +88,23 @@ CONFIGS = {
         "hsa", "hsa", 21, 30, 52, 1536, 12, 128, "bf16", static_pct=70,
         steps=8, group_pcts=(25, 25, 50), group_budgets=(8, 4, 2),
     ),
+    # The HSA schedule inside its sampling loop: Euler update after every step, the first and
+    # last step dense.
+    "hsa_loop": Config(
+        "hsa_loop", "hsa_loop", 21, 30, 52, 1536, 12, 128, "bf16", static_pct=70,
+        steps=8, group_pcts=(25, 25, 50), group_budgets=(8, 4, 2), window=1,
+    ),
     # LIPAR inter-frame sweep on a 33x45x80 grid, 75% static locations, sigma = 0.6.
     "lipar": Config(
         "lipar", "lipar", 33, 45, 80, 3072, 24, 128, "bf16", static_pct=75,
         sigma=0.6, sweep_pcts=(5, 10, 25, 50, 100),
+    ),
+    # The same clip pruned by the long/short-term mask (absolute L1 changes): a static location
+    # changes by about 24 per frame and drifts past 60 after 5-7 frames; a moving one changes
+    # by about 1200 per frame.
+    "lipar_lif": Config(
+        "lipar_lif", "lipar_lif", 33, 45, 80, 3072, 24, 128, "bf16", static_pct=75,
+        sigma=0.6, tau_short=100.0, tau_long=60.0,
     ),
 }
 
