@@ -8,8 +8,16 @@ the timed region starts.
 
 Prints ONE JSON line.  ``value`` is the effective layer throughput in
 TFLOP/s = 4 * N_active * N * head_dim * heads / step time.  Extra fields give
-tokens/s, the per-kernel times, the attention kernel's roofline and the CPU
-oracle measured on a bounded sample of the same workload.
+tokens/s, the per-kernel times (median / p10 / p90 over the timed steps), the
+attention kernel's roofline, the HBM-bound steps timed standalone against the
+HBM peak, the dense layer and the CPU oracle measured on a bounded sample of
+the same workload.
+
+Other workloads (``--workload``): ``large`` and ``tiny`` (the same step),
+``hsa`` (the T-step schedule loop), ``hsa_loop`` (the sampling loop with the
+cached Euler update and phase window), ``lipar`` (the inter-frame sweep over
+active fractions) and ``lipar_lif`` (the pass with the long/short-term mask and
+restoration); each prints its own JSON line.
 """
 
 from __future__ import annotations
@@ -34,13 +42,14 @@ ATTN_SRC = os.path.join(ROOT, "token_sparse_attention_rel_amd", "csrc", "attenti
 def parse_args(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="wan13b")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-sample-rows", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-hbm", action="store_true", help="skip the standalone HBM-kernel timings")
     ap.add_argument("--attn-schedule", choices=("split", "tile"), default="split",
                     help="attention: split the last, partly filled round of query tiles into key "
                          "ranges (default) or run one workgroup per query tile throughout")
@@ -140,26 +149,89 @@ def cpu_baseline(cfg, inp, n_sample):
     }
 
 
-def main(argv=None):
-    args = parse_args(argv)
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the pruned layer runs unsharded on a single MI355X "
-              "(multi-GPU sharding is design-only). Run with --gpus 1.", file=sys.stderr)
-        return 2
+class EventTimer:
+    """Per-repetition HIP event pairs on one stream; statistics in milliseconds."""
 
-    if args.copy_calibration:
-        return copy_calibration()
+    def __init__(self, torch, stream):
+        self.torch, self.stream, self.pairs = torch, stream, []
 
-    import torch
+    def start(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record(self.stream)
+        self.pairs.append([e, None])
 
-    import token_sparse_attention_rel_amd as tsa
-    from workloads import configs, generate
+    def stop(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record(self.stream)
+        self.pairs[-1][1] = e
 
-    cfg = configs.get_config(args.workload)
-    if cfg.kind != "step":
-        raise SystemExit("bench.py times single-step workloads (tiny, wan13b, large)")
+    def times(self):
+        return [a.elapsed_time(b) for a, b in self.pairs]
+
+
+def stats(ms):
+    """median / p10 / p90 / mean of a list of times (ms)."""
+    import numpy as np
+
+    a = np.asarray(ms, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 5), "p10": round(float(np.percentile(a, 10)), 5),
+            "p90": round(float(np.percentile(a, 90)), 5), "mean": round(float(a.mean()), 5), "reps": int(a.size)}
+
+
+def roofline_entry(kind, work, st, unit):
+    """Algorithmic work per launch over the median launch time, against the MI355X peak."""
+    t = st["median"] * 1e-3
+    if kind == "hbm":
+        achieved = work / t / 1e9
+        return {"bound": "hbm", "algorithmic_bytes": int(work), "achieved": round(achieved, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "ms": st}
+    achieved = work / t / 1e12
+    return {"bound": "mfma", "algorithmic_flop": int(work), "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS, "unit": unit, "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "ms": st}
+
+
+def hbm_kernels(tsa, torch, cfg, layer, xc, xp, reps=20):
+    """The HBM-bound steps timed standalone: a1 score (all N rows of X_cur and X_ref read),
+    a4 gather, a6 cache sync and a8 scatter of the N_a active rows (fused into the QKV and
+    attention kernels on the layer path).  The 256 MB MALL is flushed before every
+    repetition by overwriting a 512 MB buffer."""
+    stream = torch.cuda.current_stream()
+    n, d, k = cfg.n, cfg.dim, cfg.n_active
+    flush = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device=xc.device)
+    scores = torch.empty(n, dtype=torch.float32, device=xc.device)
+    ka = torch.empty(k, d, dtype=torch.bfloat16, device=xc.device)
+    va = torch.empty_like(ka)
+    kc = layer.k_cache.clone()
+    vc = layer.v_cache.clone()
+    out = layer.out.clone()
+    esz = xc.element_size()
+    ops = {
+        "a1_score": (lambda: tsa.token_scores(xc, xp, scores), 2 * n * d * esz + 4 * n),
+        "a4_gather": (lambda: tsa.gather_rows(xc, layer.idx, k, ka), k * d * (esz + 2)),
+        "a6_cache_sync": (lambda: tsa.kv_cache_sync(ka, va, layer.idx, k, kc, vc), 4 * k * d * 2),
+        "a8_scatter": (lambda: tsa.scatter_out(ka, layer.idx, k, out), 2 * k * d * 2),
+    }
+    res = {}
+    for name, (fn, nbytes) in ops.items():
+        fn()
+        tm = EventTimer(torch, stream)
+        for _ in range(reps):
+            flush.zero_()
+            tm.start()
+            fn()
+            tm.stop()
+        torch.cuda.synchronize()
+        res[name] = roofline_entry("hbm", nbytes, stats(tm.times()), "GB/s")
+    del flush
+    return res
+
+
+def bench_step(args, torch, tsa, cfg):
+    """One pruned layer step (score + top-k + compaction, QKV + cache sync, attention +
+    scatter), K timed steps; the driver's JSON line for the headline workload."""
+    from workloads import generate
+
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     inp = generate.step_inputs(cfg, args.seed)
     layer = tsa.PrunedAttentionLayer(cfg.n, cfg.dim, cfg.heads, inp["w_qkv"].to(dev), device=dev,
                                      split_attention=args.attn_schedule == "split")
@@ -174,46 +246,48 @@ def main(argv=None):
         layer.step_topk(xc, xp, k)
     torch.cuda.synchronize()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t_sel, t_qkv, t_att, t_step = (EventTimer(torch, stream) for _ in range(4))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        e = ev[i]
-        e[0].record(stream)
+    for _ in range(args.steps):
+        t_step.start()
+        t_sel.start()
         layer.select(xc, xp, k=k)
-        e[1].record(stream)
+        t_sel.stop()
+        t_qkv.start()
         tsa.qkv_active(xc, layer.idx, k, layer.w_qkv, q_out=layer.q_a, k_out=layer.k_cache,
                        v_out=layer.v_cache, out_is_cache=True, n_cache=cfg.n)
-        e[2].record(stream)
+        t_qkv.stop()
+        t_att.start()
         tsa.sparse_query_attention(layer.q_a, layer.k_cache, layer.v_cache, k, cfg.heads,
                                    cfg.head_dim, layer.out, out_rows=layer.idx, workspace=attn_ws)
-        e[3].record(stream)
+        t_att.stop()
+        t_step.stop()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    t_sel = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
-    t_qkv = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
-    t_att = sum(e[2].elapsed_time(e[3]) for e in ev) / args.steps
+    s_sel, s_qkv, s_att, s_step = (stats(t.times()) for t in (t_sel, t_qkv, t_att, t_step))
+    t_att_mean = s_att["mean"]
 
     flops = cfg.attn_flops(k)
-    dense_ms = None
+    dense = None
     if not args.no_dense:
-        dl = tsa.PrunedAttentionLayer(cfg.n, cfg.dim, cfg.heads, layer.w_qkv, device=dev)
-        dl.init_cache(xp)
-        for _ in range(2):
-            dl.step_topk(xc, xp, cfg.n)
+        # dense layer: the same QKV and attention kernels over every token, no selection
+        layer.dense_forward(xc)
         torch.cuda.synchronize()
-        nd = max(3, args.steps // 4)
-        td = time.perf_counter()
-        for _ in range(nd):
-            dl.step_topk(xc, xp, cfg.n)
+        td = EventTimer(torch, stream)
+        for _ in range(max(5, args.steps // 4)):
+            td.start()
+            layer.dense_forward(xc)
+            td.stop()
         torch.cuda.synchronize()
-        dense_ms = (time.perf_counter() - td) * 1e3 / nd
-        del dl
+        dense = stats(td.times())
+        layer.init_cache(xp)
 
-    achieved = flops / (t_att * 1e-3) / 1e12
+    hbm = None if args.no_hbm else hbm_kernels(tsa, torch, cfg, layer, xc, xp)
+    achieved = flops / (t_att_mean * 1e-3) / 1e12
     rec = {
-        "metric": METRIC,
+        "metric": METRIC if cfg.name == "wan13b" else f"pruned-attn layer TFLOP/s + tokens/s ({cfg.name})",
         "value": round(flops / (ms_step * 1e-3) / 1e12, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -240,13 +314,15 @@ def main(argv=None):
                                if attn_ws is not None else "one workgroup per query tile"),
         "tokens_per_s": round(cfg.n / (ms_step * 1e-3), 1),
         "active_tokens_per_s": round(k / (ms_step * 1e-3), 1),
+        "step_ms_events": s_step,
         "attn_tflops": round(achieved, 3),
         "attn_frac_of_mfma_peak": round(achieved / PEAK_BF16_TFLOPS, 4),
-        "kernel_ms": {"score_select_compact": round(t_sel, 4), "qkv_gather_cache_sync": round(t_qkv, 4),
-                      "attention_scatter": round(t_att, 4)},
-        "qkv_tflops": round(cfg.qkv_flops(k) / (t_qkv * 1e-3) / 1e12, 3),
-        "dense_layer_ms": None if dense_ms is None else round(dense_ms, 4),
-        "speedup_vs_dense": None if dense_ms is None else round(dense_ms / ms_step, 3),
+        "kernel_ms": {"score_select_compact": s_sel, "qkv_gather_cache_sync": s_qkv,
+                      "attention_scatter": s_att},
+        "qkv": roofline_entry("mfma", cfg.qkv_flops(k), s_qkv, "TFLOP/s"),
+        "hbm_kernels": hbm,
+        "dense_layer_ms": dense,
+        "speedup_vs_dense": None if dense is None else round(dense["median"] / s_step["median"], 3),
         "roofline": {
             "bound": "mfma",
             "kernel": ATTN_KERNELS[attn_ws is not None],
@@ -256,10 +332,267 @@ def main(argv=None):
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": attention_traffic(),
             "algorithmic_flop_per_launch": flops,
+            "launch_ms_mean_events": round(t_att_mean, 5),
         },
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_rows)
+    return rec
+
+
+def bench_hsa(args, torch, tsa, cfg):
+    """HSA schedule loop: T global steps on X_1..X_T, groups ranked once at step 0 by the
+    change between X_1 and X_0; every step syncs the cache for its active set.  Reports
+    per-step and total throughput and the same T steps run dense."""
+    from workloads import generate
+
+    dev = torch.device("cuda:0")
+    inp = generate.hsa_inputs(cfg, args.seed)
+    xs = [x.to(dev) for x in inp["xs"]]
+    layer = tsa.PrunedAttentionLayer(cfg.n, cfg.dim, cfg.heads, inp["w_qkv"].to(dev), device=dev)
+    counts, gper = cfg.group_counts(), cfg.group_periods()
+    period = torch.empty(cfg.n, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def run(timers=None, dense=False):
+        layer.init_cache(xs[0])
+        layer.select(xs[1], xs[0], k=1)
+        tsa.assign_groups(layer.scores, counts, gper, period, layer.workspace)
+        for i in range(cfg.steps):
+            if timers:
+                timers[i].start()
+            if dense:
+                layer.dense_forward(xs[i + 1])
+            else:
+                layer.select(None, periods=period, step=i)
+                layer.forward_active(xs[i + 1], tsa.hsa_active_count(counts, gper, i))
+            if timers:
+                timers[i].stop()
+
+    for _ in range(max(1, args.warmup // 4)):
+        run()
+    reps = max(3, args.steps // 8)
+    tm = [EventTimer(torch, stream) for _ in range(cfg.steps)]
+    for _ in range(reps):
+        run(tm)
+    td = [EventTimer(torch, stream) for _ in range(cfg.steps)]
+    if not args.no_dense:
+        for _ in range(reps):
+            run(td, dense=True)
+    torch.cuda.synchronize()
+    per_step, total_ms, total_flops = [], 0.0, 0
+    for i in range(cfg.steps):
+        n_act = tsa.hsa_active_count(counts, gper, i)
+        st = stats(tm[i].times())
+        total_ms += st["median"]
+        total_flops += cfg.attn_flops(n_act)
+        per_step.append({"step": i, "n_active": n_act, "ms": st,
+                         "attn_tflops_effective": round(cfg.attn_flops(n_act) / (st["median"] * 1e-3) / 1e12, 2)})
+    dense_ms = None if args.no_dense else sum(stats(t.times())["median"] for t in td)
+    return {
+        "metric": "HSA schedule loop: effective TFLOP/s and token-steps/s over T steps",
+        "value": round(total_flops / (total_ms * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "higher_is_better": True,
+        "dtype": "bf16",
+        "data": "synthetic (seeded generator; random-init projection weights)",
+        "config": {"workload": f"{cfg.name}: N={cfg.n}, D={cfg.dim}, {cfg.heads}x{cfg.head_dim}, T={cfg.steps}, "
+                               f"groups {cfg.group_pcts}% with budgets {cfg.group_budgets}", "seed": args.seed},
+        "loop_ms": round(total_ms, 4),
+        "token_steps_per_s": round(cfg.n * cfg.steps / (total_ms * 1e-3), 1),
+        "per_step": per_step,
+        "dense_loop_ms": None if dense_ms is None else round(dense_ms, 4),
+        "speedup_vs_dense": None if dense_ms is None else round(dense_ms / total_ms, 3),
+        "repetitions": reps,
+    }
+
+
+def bench_hsa_loop(args, torch, tsa, cfg):
+    """The sampling loop with the cached Euler update and the phase window (fp32 state)."""
+    from workloads import generate
+
+    dev = torch.device("cuda:0")
+    inp = generate.hsa_inputs(cfg, args.seed)
+    x0, x1 = inp["xs"][0].to(dev), inp["xs"][1].to(dev)
+    layer = tsa.PrunedAttentionLayer(cfg.n, cfg.dim, cfg.heads, inp["w_qkv"].to(dev), device=dev)
+    counts, gper = cfg.group_counts(), cfg.group_periods()
+    sig = cfg.sigmas()
+    period = torch.empty(cfg.n, dtype=torch.uint8, device=dev)
+    layer.select(x1, x0, k=1)
+    tsa.assign_groups(layer.scores, counts, gper, period, layer.workspace)
+    stream = torch.cuda.current_stream()
+    x = torch.empty(cfg.n, cfg.dim, dtype=torch.float32, device=dev)
+
+    def run(window, t_loop=None):
+        x.copy_(x0)
+        if t_loop:
+            t_loop.start()
+        layer.hsa_run(x, period, sig, window, counts, gper)
+        if t_loop:
+            t_loop.stop()
+
+    run(cfg.window)
+    reps = max(3, args.steps // 8)
+    t_loop = EventTimer(torch, stream)
+    for _ in range(reps):
+        run(cfg.window, t_loop)
+    t_dense = EventTimer(torch, stream)
+    if not args.no_dense:
+        for _ in range(reps):
+            run(cfg.steps, t_dense)
+    # the Euler kernel alone: read x (fp32) and v_hat (bf16), write x
+    t_eu = EventTimer(torch, stream)
+    flush = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device=dev)
+    for _ in range(20):
+        flush.zero_()
+        t_eu.start()
+        tsa.euler_update(x, layer.out, -1.0 / cfg.steps)
+        t_eu.stop()
+    torch.cuda.synchronize()
+    loop = stats(t_loop.times())
+    counts_per_step = [cfg.n if (i < cfg.window or i >= cfg.steps - cfg.window)
+                       else tsa.hsa_active_count(counts, gper, i) for i in range(cfg.steps)]
+    flops = sum(cfg.attn_flops(c) for c in counts_per_step)
+    dense = None if args.no_dense else stats(t_dense.times())
+    return {
+        "metric": "HSA sampling loop (Euler update, phase window): effective TFLOP/s over T steps",
+        "value": round(flops / (loop["median"] * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "higher_is_better": True,
+        "dtype": "bf16 (fp32 latent state)",
+        "data": "synthetic (seeded generator; random-init projection weights)",
+        "config": {"workload": f"{cfg.name}: N={cfg.n}, D={cfg.dim}, {cfg.heads}x{cfg.head_dim}, T={cfg.steps}, "
+                               f"window={cfg.window}, linear sigmas, groups {cfg.group_pcts}% budgets "
+                               f"{cfg.group_budgets}", "seed": args.seed},
+        "active_per_step": counts_per_step,
+        "loop_ms": loop,
+        "token_steps_per_s": round(cfg.n * cfg.steps / (loop["median"] * 1e-3), 1),
+        "dense_loop_ms": dense,
+        "speedup_vs_dense": None if dense is None else round(dense["median"] / loop["median"], 3),
+        "euler": roofline_entry("hbm", cfg.n * cfg.dim * (4 + 2 + 4), stats(t_eu.times()), "GB/s"),
+    }
+
+
+def bench_lipar(args, torch, tsa, cfg):
+    """LIPAR inter-frame sweep: one pruned pass over the whole clip per active fraction."""
+    from workloads import generate
+
+    dev = torch.device("cuda:0")
+    inp = generate.lipar_inputs(cfg, args.seed)
+    x = inp["x"].to(dev)
+    layer = tsa.PrunedAttentionLayer(cfg.n, cfg.dim, cfg.heads, inp["w_qkv"].to(dev), device=dev)
+    stream = torch.cuda.current_stream()
+    points = []
+    reps = max(3, args.steps // 10)
+    for p, (pct, k) in enumerate(zip(cfg.sweep_pcts, cfg.sweep_counts())):
+        eps = generate.lipar_eps(cfg, args.seed, p).to(dev)
+        layer.step_lipar(x, eps, cfg.hw, k, cfg.sigma)
+        tm = EventTimer(torch, stream)
+        for _ in range(reps):
+            tm.start()
+            layer.step_lipar(x, eps, cfg.hw, k, cfg.sigma)
+            tm.stop()
+        torch.cuda.synchronize()
+        st = stats(tm.times())
+        fl = cfg.attn_flops(k)
+        points.append({"active_pct": pct, "n_active": k, "ms": st,
+                       "attn_tflops_effective": round(fl / (st["median"] * 1e-3) / 1e12, 2),
+                       "tokens_per_s": round(cfg.n / (st["median"] * 1e-3), 1)})
+        del eps
+    full = points[-1]["ms"]["median"]
+    for pt in points:
+        pt["speedup_vs_100pct"] = round(full / pt["ms"]["median"], 3)
+    return {
+        "metric": "LIPAR inter-frame sweep: pass time, effective TFLOP/s and tokens/s per active fraction",
+        "value": points[0]["attn_tflops_effective"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "higher_is_better": True,
+        "dtype": "bf16",
+        "data": "synthetic (seeded generator; random-init projection weights)",
+        "config": {"workload": f"{cfg.name}: F={cfg.frames} H={cfg.height} W={cfg.width} -> N={cfg.n}, "
+                               f"D={cfg.dim}, {cfg.heads}x{cfg.head_dim}, sigma={cfg.sigma}", "seed": args.seed},
+        "points": points,
+        "repetitions": reps,
+    }
+
+
+def bench_lipar_lif(args, torch, tsa, cfg):
+    """LIPAR pass with the long/short-term mask and the restoration of pruned frames."""
+    from workloads import generate
+
+    dev = torch.device("cuda:0")
+    inp = generate.lipar_inputs(cfg, args.seed)
+    x = inp["x"].to(dev)
+    eps = generate.lipar_eps(cfg, args.seed, 0).to(dev)
+    layer = tsa.PrunedAttentionLayer(cfg.n, cfg.dim, cfg.heads, inp["w_qkv"].to(dev), device=dev)
+    stream = torch.cuda.current_stream()
+    k = layer.step_lipar_lif(x, eps, cfg.frames, cfg.hw, cfg.tau_short, cfg.tau_long, cfg.sigma)
+    reps = max(3, args.steps // 10)
+    t_pass = EventTimer(torch, stream)
+    for _ in range(reps):
+        t_pass.start()
+        layer.step_lipar_lif(x, eps, cfg.frames, cfg.hw, cfg.tau_short, cfg.tau_long, cfg.sigma)
+        t_pass.stop()
+    mask = torch.empty(cfg.n, dtype=torch.uint8, device=dev)
+    flush = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device=dev)
+    t_mask, t_rest = EventTimer(torch, stream), EventTimer(torch, stream)
+    for _ in range(20):
+        flush.zero_()
+        t_mask.start()
+        tsa.lif_mask(x, cfg.frames, cfg.hw, cfg.tau_short, cfg.tau_long, mask)
+        t_mask.stop()
+        flush.zero_()
+        t_rest.start()
+        tsa.restore_frames(layer.out, mask, cfg.frames, cfg.hw)
+        t_rest.stop()
+    torch.cuda.synchronize()
+    st = stats(t_pass.times())
+    fl = cfg.attn_flops(k)
+    row = cfg.dim * 2
+    return {
+        "metric": "LIPAR pass with long/short-term mask + restoration: effective TFLOP/s and tokens/s",
+        "value": round(fl / (st["median"] * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "higher_is_better": True,
+        "dtype": "bf16",
+        "data": "synthetic (seeded generator; random-init projection weights)",
+        "config": {"workload": f"{cfg.name}: F={cfg.frames} H={cfg.height} W={cfg.width} -> N={cfg.n}, "
+                               f"D={cfg.dim}, {cfg.heads}x{cfg.head_dim}, abs L1 thresholds short "
+                               f"{cfg.tau_short} / long {cfg.tau_long}, sigma={cfg.sigma}", "seed": args.seed},
+        "n_active": k,
+        "active_frac": round(k / cfg.n, 4),
+        "pass_ms": st,
+        "tokens_per_s": round(cfg.n / (st["median"] * 1e-3), 1),
+        "lif_mask": roofline_entry("hbm", cfg.n * row + cfg.n, stats(t_mask.times()), "GB/s"),
+        "restore": roofline_entry("hbm", cfg.n * row + cfg.n, stats(t_rest.times()), "GB/s"),
+        "repetitions": reps,
+    }
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the pruned layer runs unsharded on a single MI355X "
+              "(multi-GPU sharding is design-only). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    if args.copy_calibration:
+        return copy_calibration()
+
+    import torch
+
+    import token_sparse_attention_rel_amd as tsa
+    from workloads import configs
+
+    cfg = configs.get_config(args.workload)
+    torch.cuda.set_device(0)
+    fn = {"step": bench_step, "hsa": bench_hsa, "hsa_loop": bench_hsa_loop, "lipar": bench_lipar,
+          "lipar_lif": bench_lipar_lif}[cfg.kind]
+    rec = fn(args, torch, tsa, cfg)
     print(json.dumps(rec), flush=True)
     return 0
 

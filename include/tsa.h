@@ -112,6 +112,15 @@ tsa_status tsa_select_active(const void* x_cur, const void* x_ref, int64_t ref_r
                              size_t workspace_bytes, void* stream);
 
 /*
+ * a1 alone (for measurement and for callers that select on the host): the
+ * per-token change scores of tsa_select_active, with the same reference-row
+ * rules and the same arithmetic, written to scores_out (device f32[n_rows]).
+ * Errors: INVALID_ARG, SHAPE, DTYPE, ALIGNMENT, HIP.
+ */
+tsa_status tsa_token_scores(const void* x_cur, const void* x_ref, int64_t ref_row_offset, int64_t n_rows,
+                            int64_t dim, int dtype, int score_kind, float* scores_out, void* stream);
+
+/*
  * [HSA] §2.1: partition the tokens into disjoint groups by score rank
  * (highest score first, ties in ascending token order): group g takes the
  * next group_counts[g] tokens and each of its tokens gets the activity period

@@ -33,6 +33,7 @@ from ._binding import (
     select_workspace_bytes,
     sparse_query_attention,
     status_string,
+    token_scores,
 )
 from .layer import PrunedAttentionLayer, hsa_active_count
 
@@ -42,6 +43,6 @@ __all__ = [
     "BF16", "F32", "SCORE_ABS_L1", "SCORE_REL_L1", "SELECT_MASK", "SELECT_SCHEDULE",
     "SELECT_THRESHOLD", "SELECT_TOPK", "TsaError", "abi_version", "assign_groups", "attention_workspace_bytes", "euler_update", "gather_rows",
     "kv_cache_sync", "lib", "lib_path", "lif_mask", "qkv_active", "restore_frames", "scatter_out", "select_active",
-    "select_workspace_bytes", "sparse_query_attention", "status_string",
+    "select_workspace_bytes", "sparse_query_attention", "status_string", "token_scores",
     "PrunedAttentionLayer", "hsa_active_count",
 ]

@@ -44,6 +44,7 @@ _SIGNATURES = {
     "tsa_attention_workspace_bytes": (_size, [_i64, _i64, _int, _int]),
     "tsa_scatter_out": (_int, [_vp, _vp, _i64, _vp, _i64, _i64, _vp]),
     "tsa_gather_rows": (_int, [_vp, _i64, _vp, _i64, _i64, _vp, _i64, _f32, _vp, _vp]),
+    "tsa_token_scores": (_int, [_vp, _vp, _i64, _i64, _i64, _int, _int, _vp, _vp]),
     "tsa_euler_update": (_int, [_vp, _int, _vp, _i64, _i64, _f32, _vp]),
     "tsa_lif_mask": (_int, [_vp, _int, _i64, _i64, _i64, _int, _f32, _f32, _vp, _vp, _vp, _vp]),
     "tsa_restore_frames": (_int, [_vp, _int, _vp, _i64, _i64, _i64, _vp]),
@@ -237,3 +238,11 @@ def restore_frames(buf, mask, frames, hw, stream=None):
     st = lib().tsa_restore_frames(_ptr(buf), _dtype_code(buf), _ptr(mask), int(frames), int(hw),
                                   int(buf.shape[1]), _stream(stream))
     _check("tsa_restore_frames", st)
+
+
+def token_scores(x_cur, x_ref, scores_out, *, ref_row_offset=0, score_kind=SCORE_REL_L1, stream=None):
+    """a1 alone (tsa_token_scores)."""
+    st = lib().tsa_token_scores(_ptr(x_cur), _ptr(x_ref), int(ref_row_offset), int(x_cur.shape[0]),
+                                int(x_cur.shape[1]), _dtype_code(x_cur), int(score_kind), _ptr(scores_out),
+                                _stream(stream))
+    _check("tsa_token_scores", st)

@@ -88,6 +88,18 @@ tsa_status tsa_select_active(const void* x_cur, const void* x_ref, int64_t ref_r
                                      n_active_out, nullptr, 0, s));
 }
 
+tsa_status tsa_token_scores(const void* x_cur, const void* x_ref, int64_t ref_row_offset, int64_t n_rows,
+                            int64_t dim, int dtype, int score_kind, float* scores_out, void* stream) {
+  if (!x_cur || !scores_out) return TSA_ERR_INVALID_ARG;
+  if (score_kind != TSA_SCORE_REL_L1 && score_kind != TSA_SCORE_ABS_L1) return TSA_ERR_INVALID_ARG;
+  if (dtype != TSA_F32 && dtype != TSA_BF16) return TSA_ERR_DTYPE;
+  if (n_rows < 0 || n_rows > kMaxRows || dim <= 0 || dim % 8 != 0) return TSA_ERR_SHAPE;
+  if (!aligned16(x_cur) || (x_ref && !aligned16(x_ref)) || !aligned16(scores_out)) return TSA_ERR_ALIGNMENT;
+  if (n_rows == 0) return TSA_OK;
+  return from_hip(tsa::launch_scores(x_cur, x_ref, ref_row_offset, n_rows, dim, dtype,
+                                     score_kind == TSA_SCORE_REL_L1, scores_out, as_stream(stream)));
+}
+
 tsa_status tsa_assign_groups(const float* scores, int64_t n, int n_groups,
                              const int64_t* group_counts, const uint8_t* group_periods,
                              uint8_t* period_out, void* workspace, size_t workspace_bytes,
