@@ -188,19 +188,20 @@ __device__ __forceinline__ void attend_segment(const AttnArgs& a, uint16_t* ks_b
   f32x16 acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+  // V^T operand of the MFMA for 16-key chunk ch and 32-wide dim block db of a V tile.
+  auto v_frag = [&](const uint16_t* vt, int ch, int db) {
+    const uint16_t* vp = vt + 16 * ch * LDV + 32 * db + v_off;
+    const v4i16 lo = ds_read_tr16(vp);
+    const v4i16 hi4 = ds_read_tr16(vp + 8 * LDV);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
   // O^T[dim, query] += V^T[dim, key] P^T[key, query] over one 32-key tile (two 16-key chunks).
   auto pv = [&](const uint16_t* vt, const bf16x8* pf) {
 #pragma unroll
     for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const uint16_t* vp = vt + 16 * ch * LDV + 32 * db + v_off;
-        const v4i16 lo = ds_read_tr16(vp);
-        const v4i16 hi4 = ds_read_tr16(vp + 8 * LDV);
-        const bf16x8 vf = __builtin_bit_cast(
-            bf16x8, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ch], acc[db], 0, 0, 0);
-      }
+      for (int db = 0; db < NDB; ++db)
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag(vt, ch, db), pf[ch], acc[db], 0, 0, 0);
   };
 
   float m_run = -__builtin_inff();
@@ -222,14 +223,27 @@ __device__ __forceinline__ void attend_segment(const AttnArgs& a, uint16_t* ks_b
   __syncthreads();  // every wave is done with K(t0) before K(t0+2) overwrites it
 
   bf16x8 p_prev[2];
-  // Iteration t: MFMA work PV(t-1) and QK(t+1) interleaved with the softmax of
-  // tile t on the VALU; then stage V(t) and K(t+2) and fetch V(t+1) and K(t+3).
+  // Iteration t: the softmax of tile t on the VALU, interleaved with the MFMA work
+  // PV(t-1) and QK(t+1); then stage V(t) and K(t+2) and fetch V(t+1) and K(t+3).
   // A buffer is rewritten only after the barrier that follows its last read.
   auto iteration = [&](long t, auto has_prev, auto has_next, auto may_mask) {
     const int b = static_cast<int>((t - t0) & 1);
-    f32x16 s_next;
-    if constexpr (decltype(has_prev)::value) pv(vs(b ^ 1), p_prev);
-    if constexpr (decltype(has_next)::value) s_next = qk(ks(b ^ 1));
+    // LDS reads of this iteration's MFMA operands go out first, so that their
+    // latency (and that of the barrier just passed) is covered by the softmax.
+    const uint16_t* kt = ks(b ^ 1);
+    const uint16_t* vt = vs(b ^ 1);
+    bf16x8 kf[NM];
+    bf16x8 vf[2][NDB];
+    if constexpr (decltype(has_next)::value) {
+#pragma unroll
+      for (int m = 0; m < NM; ++m) kf[m] = *reinterpret_cast<const bf16x8*>(&kt[l32 * LDK + 16 * m + 8 * hi]);
+    }
+    if constexpr (decltype(has_prev)::value) {
+#pragma unroll
+      for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) vf[ch][db] = v_frag(vt, ch, db);
+    }
 
     float mx = -__builtin_inff();
 #pragma unroll
@@ -252,10 +266,23 @@ __device__ __forceinline__ void attend_segment(const AttnArgs& a, uint16_t* ks_b
     {
       // Keep the softmax in this block: its results are consumed only in the next
       // iteration, and left alone the compiler sinks it past the barrier, where it
-      // can no longer overlap the MFMAs above.  (An empty asm that reads them.)
+      // can no longer overlap the MFMAs below.  (An empty asm that reads them.)
       const u32x4 p0 = __builtin_bit_cast(u32x4, pf[0]), p1 = __builtin_bit_cast(u32x4, pf[1]);
       asm volatile("" ::"v"(p0[0]), "v"(p0[1]), "v"(p0[2]), "v"(p0[3]), "v"(p1[0]), "v"(p1[1]),
                    "v"(p1[2]), "v"(p1[3]), "v"(l_run), "v"(alpha));
+    }
+    f32x16 s_next;
+    if constexpr (decltype(has_prev)::value) {
+#pragma unroll
+      for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ch][db], p_prev[ch], acc[db], 0, 0, 0);
+    }
+    if constexpr (decltype(has_next)::value) {
+      s_next = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qf[0], f32x16{}, 0, 0, 0);
+#pragma unroll
+      for (int m = 1; m < NM; ++m) s_next = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[m], qf[m], s_next, 0, 0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (decltype(may_mask)::value) mask_tail(s_next, (t + 1) * BN);
