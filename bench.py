@@ -194,7 +194,8 @@ def hbm_kernels(tsa, torch, cfg, layer, xc, xp, reps=20):
     """The HBM-bound steps timed standalone: a1 score (all N rows of X_cur and X_ref read),
     a4 gather, a6 cache sync and a8 scatter of the N_a active rows (fused into the QKV and
     attention kernels on the layer path).  The 256 MB MALL is flushed before every
-    repetition by overwriting a 512 MB buffer."""
+    repetition by reading a 512 MB buffer (reading, not writing: dirty flush lines
+    would be written back to HBM during the timed kernel)."""
     stream = torch.cuda.current_stream()
     n, d, k = cfg.n, cfg.dim, cfg.n_active
     flush = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device=xc.device)
@@ -216,7 +217,7 @@ def hbm_kernels(tsa, torch, cfg, layer, xc, xp, reps=20):
         fn()
         tm = EventTimer(torch, stream)
         for _ in range(reps):
-            flush.zero_()
+            flush.max()
             tm.start()
             fn()
             tm.stop()
@@ -445,7 +446,7 @@ def bench_hsa_loop(args, torch, tsa, cfg):
     t_eu = EventTimer(torch, stream)
     flush = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device=dev)
     for _ in range(20):
-        flush.zero_()
+        flush.max()
         t_eu.start()
         tsa.euler_update(x, layer.out, -1.0 / cfg.steps)
         t_eu.stop()
@@ -540,11 +541,11 @@ def bench_lipar_lif(args, torch, tsa, cfg):
     flush = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device=dev)
     t_mask, t_rest = EventTimer(torch, stream), EventTimer(torch, stream)
     for _ in range(20):
-        flush.zero_()
+        flush.max()
         t_mask.start()
         tsa.lif_mask(x, cfg.frames, cfg.hw, cfg.tau_short, cfg.tau_long, mask)
         t_mask.stop()
-        flush.zero_()
+        flush.max()
         t_rest.start()
         tsa.restore_frames(layer.out, mask, cfg.frames, cfg.hw)
         t_rest.stop()

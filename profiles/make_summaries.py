@@ -43,7 +43,7 @@ def trace_summary(d):
         "# (N=32760 tokens, D=1536, 12 heads x 128, 30% active = 9828 queries)",
         "# command (repository root, one MI355X):",
         "#   rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_trace -o run -- \\",
-        "#       python3 bench.py --steps 10 --warmup 3 --no-cpu-baseline --no-dense",
+        "#       python3 bench.py --steps 10 --warmup 3 --no-cpu-baseline --no-dense --no-hbm",
         "# summary written by: python profiles/make_summaries.py gpurun_out",
         "",
         f"{'kernel':48s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>6s}",
@@ -56,7 +56,7 @@ def trace_summary(d):
             f"#   -> {FLOP / (avg_t * 1e-6) / 1e12:.1f} TFLOP/s = {FLOP / (avg_t * 1e-6) / 1e12 / 2500 * 100:.1f}% of 2500 TFLOP/s"]
     if bench:
         out.append(f"# bench.py under the profiler (HIP events on the launch stream): attention "
-                   f"{bench['kernel_ms']['attention_scatter']*1e3:.1f} us, roofline.achieved {bench['roofline']['achieved']} TFLOP/s")
+                   f"{bench['kernel_ms']['attention_scatter']['mean']*1e3:.1f} us (mean; median {bench['kernel_ms']['attention_scatter']['median']*1e3:.1f} us), roofline.achieved {bench['roofline']['achieved']} TFLOP/s")
     return "\n".join(out) + "\n"
 
 
@@ -81,8 +81,8 @@ def traffic_summary(d):
     out = [
         "# HBM traffic per launch from rocprofv3 counters, wan13b pruned layer step",
         "# commands (repository root, one MI355X; one counter per run):",
-        "#   timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-dense",
-        "#   timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-dense",
+        "#   timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-dense --no-hbm",
+        "#   timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-dense --no-hbm",
         "# calibration: the same two counters over `python3 bench.py --copy-calibration` (a plain 1 GiB",
         "#   device copy, __amd_rocclr_copyBuffer, reading and writing exactly 1048576 KiB per launch):",
         f"#   FETCH_SIZE reads {cf:.1f} KiB per copy -> scale {sf:.4f};  WRITE_SIZE reads {cw:.1f} KiB -> scale {sw:.4f}",
@@ -104,11 +104,38 @@ def traffic_summary(d):
     return "\n".join(out) + "\n"
 
 
+def stats_summary(d, sub, title, command):
+    """Per-kernel statistics of one rocprofv3 --kernel-trace --stats run."""
+    stats = list(csv.DictReader(open(os.path.join(d, sub, "run_kernel_stats.csv"))))
+    out = [f"# rocprofv3 kernel-trace summary: {title}", "# command (repository root, one MI355X):",
+           f"#   {command}", "# summary written by: python profiles/make_summaries.py gpurun_out", "",
+           f"{'kernel':48s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>6s}"]
+    for r in stats:
+        out.append(f"{_short(r['Name'])[:48]:48s} {r['Calls']:>6s} {float(r['AverageNs'])/1e3:10.1f} "
+                   f"{float(r['MinNs'])/1e3:10.1f} {float(r['MaxNs'])/1e3:10.1f} {float(r['Percentage']):6.2f}")
+    return "\n".join(out) + "\n"
+
+
+EXTRA = [
+    ("prof_hsa_loop", "hsa_loop_wan13b_kernel_trace.txt",
+     "HSA sampling loop (Euler update, phase window), N=32760, D=1536, 12 x 128, T=8",
+     "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_hsa_loop -o run -- "
+     "python3 bench.py --workload hsa_loop --steps 8 --warmup 1 --no-dense"),
+    ("prof_lipar_lif", "lipar_lif_kernel_trace.txt",
+     "LIPAR pass with the long/short-term mask + restoration, 33x45x80 -> N=118800, D=3072, 24 x 128",
+     "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_lipar_lif -o run -- "
+     "python3 bench.py --workload lipar_lif --steps 10 --warmup 1"),
+]
+
+
 def main(argv):
     d = argv[1] if len(argv) > 1 else "gpurun_out"
     here = os.path.dirname(os.path.abspath(__file__))
     open(os.path.join(here, "layer_step_wan13b_kernel_trace.txt"), "w").write(trace_summary(d))
     open(os.path.join(here, "attention_wan13b_traffic.txt"), "w").write(traffic_summary(d))
+    for sub, fname, title, cmd in EXTRA:
+        if os.path.exists(os.path.join(d, sub, "run_kernel_stats.csv")):
+            open(os.path.join(here, fname), "w").write(stats_summary(d, sub, title, cmd))
     return 0
 
 

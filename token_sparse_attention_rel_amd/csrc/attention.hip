@@ -38,11 +38,25 @@ constexpr int kMaxPieces = 64;
 constexpr int kMinPieceTiles = 4;
 constexpr int kMaxPieceSlots = 6;
 
-// Waves per workgroup (32 queries each): 8 for head_dim 128, so every thread
-// stages one 16-byte chunk of K and of V per tile and one K/V tile in LDS feeds
-// 256 queries; 4 for head_dim 64 (a 32 x 64 tile has 256 chunks).
+// Waves per workgroup and 32-query blocks per wave.  head_dim 128: 8 waves of
+// 32 queries, two per SIMD, so that one wave's softmax runs while the other's
+// MFMAs do; every thread then stages one 16-byte chunk of K and of V per tile.
+// (Four waves of two blocks each -- one wave per SIMD with up to 512 VGPRs, each
+// K/V fragment feeding two MFMAs -- measured about 9% slower on MI355X: a lone
+// wave cannot hide its own LDS and MFMA latencies.)  head_dim 64: 4 waves of 32
+// queries (a 32 x 64 tile has 256 16-byte chunks).  A workgroup covers 256
+// (128) queries of one head.
 template <int HD>
 constexpr int attn_waves() { return HD == 128 ? 8 : 4; }
+template <int HD>
+constexpr int attn_qblocks() { return 1; }
+template <int HD>
+constexpr int attn_blocks() { return attn_waves<HD>() * attn_qblocks<HD>(); }
+template <int HD>
+constexpr int attn_rows() { return 32 * attn_blocks<HD>(); }
+// Resident workgroups per CU the register budget is sized for.
+template <int HD>
+constexpr int attn_min_blocks() { return 2; }
 
 struct AttnArgs {
   const uint16_t* q;
@@ -84,9 +98,10 @@ template <bool B>
 using Flag = std::integral_constant<bool, B>;
 
 // Partial result of one segment, laid out as the registers hold it (lane fastest):
-// O^T accumulators [wave][NDB*16][64], then the shift m and the sum l [wave][64].
+// O^T accumulators [block][NDB*16][64], then the shift m and the sum l [block][64],
+// block = wave * (blocks per wave) + block of the wave.
 template <int HD>
-constexpr long attn_piece_floats() { return attn_waves<HD>() * 64L * (HD / 32 * 16 + 2); }
+constexpr long attn_piece_floats() { return attn_blocks<HD>() * 64L * (HD / 32 * 16 + 2); }
 
 // Keys [t0*BN, t1*BN) of query tile `tile` (head-major numbering).  part == nullptr:
 // normalise and write the bf16 output rows (+ LSE); otherwise write the partial
@@ -96,8 +111,10 @@ template <int HD>
 __device__ __forceinline__ void attend_segment(const AttnArgs& a, uint16_t* ks_base, uint16_t* vs_base,
                                                long tile, long t0, long t1, float* part) {
   constexpr int BN = kAttnBN;
-  constexpr int NT = 64 * attn_waves<HD>();  // threads
-  constexpr int BM = 32 * attn_waves<HD>();  // queries per workgroup
+  constexpr int NW = attn_waves<HD>();
+  constexpr int QB = attn_qblocks<HD>();
+  constexpr int NT = 64 * NW;             // threads
+  constexpr int BM = attn_rows<HD>();     // queries per workgroup
   // K rows: stride HD+8 elements (16-byte reads down a column hit distinct banks).
   // V rows: stride HD+32 elements = 64 mod 256 bytes, so the four rows touched by
   // a 32-lane half of a transposing read land on disjoint banks.
@@ -121,15 +138,18 @@ __device__ __forceinline__ void attend_segment(const AttnArgs& a, uint16_t* ks_b
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
 
-  const long qrow = qt * BM + wave * 32 + l32;
-  const bool qvalid = qrow < a.n_q;
-  bf16x8 qf[NM];
-  {
+  // Block qb of this wave holds queries qrow0 + 32 * qb.
+  const long qrow0 = qt * BM + wave * 32 * QB + l32;
+  bf16x8 qf[QB][NM];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const long qrow = qrow0 + 32 * qb;
+    const bool qvalid = qrow < a.n_q;
     const uint16_t* qp = a.q + (qvalid ? qrow : 0) * D + head * HD + 8 * hi;
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
       u32x4 t = qvalid ? *reinterpret_cast<const u32x4*>(qp + 16 * m) : u32x4{0u, 0u, 0u, 0u};
-      qf[m] = __builtin_bit_cast(bf16x8, t);
+      qf[qb][m] = __builtin_bit_cast(bf16x8, t);
     }
   }
 
@@ -163,21 +183,27 @@ __device__ __forceinline__ void attend_segment(const AttnArgs& a, uint16_t* ks_b
     for (int j = 0; j < NCH; ++j) *reinterpret_cast<u32x4*>(buf + off[j]) = r[j];
   };
 
-  // S^T block (32 keys x 32 queries): keys 8*(r/4) + 4*hi + r%4 (r = 0..15), query l32.
-  auto qk = [&](const uint16_t* kt) {
-    f32x16 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-        *reinterpret_cast<const bf16x8*>(&kt[l32 * LDK + 8 * hi]), qf[0], f32x16{}, 0, 0, 0);
-#pragma unroll
-    for (int m = 1; m < NM; ++m)
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          *reinterpret_cast<const bf16x8*>(&kt[l32 * LDK + 16 * m + 8 * hi]), qf[m], s, 0, 0, 0);
-    return s;
+  // K operand of step m (dims 16m..16m+15) for S^T = K Q^T.
+  auto k_frag = [&](const uint16_t* kt, int m) {
+    return *reinterpret_cast<const bf16x8*>(&kt[l32 * LDK + 16 * m + 8 * hi]);
   };
-  auto mask_tail = [&](f32x16& s, long kv0) {
+  // S^T blocks (32 keys x 32 queries): keys 8*(r/4) + 4*hi + r%4 (r = 0..15), query l32.
+  auto qk = [&](const uint16_t* kt, f32x16* s) {
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const bf16x8 kf = k_frag(kt, m);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][m], m == 0 ? f32x16{} : s[qb], 0, 0, 0);
+    }
+  };
+  auto mask_tail = [&](f32x16* s, long kv0) {
     if (kv0 + BN > n_kv) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (kv0 + 8 * (r >> 2) + 4 * hi + (r & 3) >= n_kv) s[r] = -__builtin_inff();
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kv0 + 8 * (r >> 2) + 4 * hi + (r & 3) >= n_kv) s[qb][r] = -__builtin_inff();
     }
   };
 
@@ -185,9 +211,11 @@ __device__ __forceinline__ void attend_segment(const AttnArgs& a, uint16_t* ks_b
   // second read) and dims 16*(g%2) + 0..15 of each 32-wide dim block.
   const int grp = lane >> 4, gl = lane & 15;
   const int v_off = (4 * (grp >> 1) + (gl >> 2)) * LDV + 16 * (grp & 1) + 4 * (gl & 3);
-  f32x16 acc[NDB];
+  f32x16 acc[QB][NDB];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[qb][db] = f32x16{};
   // V^T operand of the MFMA for 16-key chunk ch and 32-wide dim block db of a V tile.
   auto v_frag = [&](const uint16_t* vt, int ch, int db) {
     const uint16_t* vp = vt + 16 * ch * LDV + 32 * db + v_off;
@@ -195,19 +223,14 @@ __device__ __forceinline__ void attend_segment(const AttnArgs& a, uint16_t* ks_b
     const v4i16 hi4 = ds_read_tr16(vp + 8 * LDV);
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  // O^T[dim, query] += V^T[dim, key] P^T[key, query] over one 32-key tile (two 16-key chunks).
-  auto pv = [&](const uint16_t* vt, const bf16x8* pf) {
-#pragma unroll
-    for (int ch = 0; ch < 2; ++ch)
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag(vt, ch, db), pf[ch], acc[db], 0, 0, 0);
-  };
 
-  float m_run = -__builtin_inff();
-  float l_run = 0.f;
+  float m_run[QB], l_run[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = -__builtin_inff();
+    l_run[qb] = 0.f;
+  }
   const float c = a.scale_log2;
-  const long n_t = (n_kv + BN - 1) / BN;
 
   // Prologue: K tiles t0 and t0+1 in LDS, S of tile t0; registers hold K(t0+2), V(t0).
   u32x4 kr[NCH], vr[NCH];
@@ -218,11 +241,12 @@ __device__ __forceinline__ void attend_segment(const AttnArgs& a, uint16_t* ks_b
   __syncthreads();
   gload(kr, krs, (t0 + 2) * BN);
   gload(vr, vrs, t0 * BN);
-  f32x16 s_cur = qk(ks(0));
+  f32x16 s_cur[QB];
+  qk(ks(0), s_cur);
   mask_tail(s_cur, t0 * BN);
   __syncthreads();  // every wave is done with K(t0) before K(t0+2) overwrites it
 
-  bf16x8 p_prev[2];
+  bf16x8 p_prev[QB][2];
   // Iteration t: the softmax of tile t on the VALU, interleaved with the MFMA work
   // PV(t-1) and QK(t+1); then stage V(t) and K(t+2) and fetch V(t+1) and K(t+3).
   // A buffer is rewritten only after the barrier that follows its last read.
@@ -236,7 +260,7 @@ __device__ __forceinline__ void attend_segment(const AttnArgs& a, uint16_t* ks_b
     bf16x8 vf[2][NDB];
     if constexpr (decltype(has_next)::value) {
 #pragma unroll
-      for (int m = 0; m < NM; ++m) kf[m] = *reinterpret_cast<const bf16x8*>(&kt[l32 * LDK + 16 * m + 8 * hi]);
+      for (int m = 0; m < NM; ++m) kf[m] = k_frag(kt, m);
     }
     if constexpr (decltype(has_prev)::value) {
 #pragma unroll
@@ -245,44 +269,51 @@ __device__ __forceinline__ void attend_segment(const AttnArgs& a, uint16_t* ks_b
         for (int db = 0; db < NDB; ++db) vf[ch][db] = v_frag(vt, ch, db);
     }
 
-    float mx = -__builtin_inff();
+    bf16x8 pf[QB][2];
+    bool upd[QB];
+    float alpha[QB];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float cand = mx * c;
-    const bool upd = cand > m_run + kLazyMax;
-    const float m_new = upd ? cand : m_run;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    bf16x8 pf[2];
-    float psum = 0.f;
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = -__builtin_inff();
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(s_cur[r], c, -m_new));
-      psum += p;
-      pf[r >> 3][r & 7] = static_cast<__bf16>(p);
-    }
-    l_run = fmaf(l_run, alpha, psum);
-    {
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[qb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float cand = mx * c;
+      upd[qb] = cand > m_run[qb] + kLazyMax;
+      const float m_new = upd[qb] ? cand : m_run[qb];
+      alpha[qb] = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+      m_run[qb] = m_new;
+      float psum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s_cur[qb][r], c, -m_new));
+        psum += p;
+        pf[qb][r >> 3][r & 7] = static_cast<__bf16>(p);
+      }
+      l_run[qb] = fmaf(l_run[qb], alpha[qb], psum);
       // Keep the softmax in this block: its results are consumed only in the next
       // iteration, and left alone the compiler sinks it past the barrier, where it
       // can no longer overlap the MFMAs below.  (An empty asm that reads them.)
-      const u32x4 p0 = __builtin_bit_cast(u32x4, pf[0]), p1 = __builtin_bit_cast(u32x4, pf[1]);
+      const u32x4 p0 = __builtin_bit_cast(u32x4, pf[qb][0]), p1 = __builtin_bit_cast(u32x4, pf[qb][1]);
       asm volatile("" ::"v"(p0[0]), "v"(p0[1]), "v"(p0[2]), "v"(p0[3]), "v"(p1[0]), "v"(p1[1]),
-                   "v"(p1[2]), "v"(p1[3]), "v"(l_run), "v"(alpha));
+                   "v"(p1[2]), "v"(p1[3]), "v"(l_run[qb]), "v"(alpha[qb]));
     }
-    f32x16 s_next;
+    f32x16 s_next[QB];
     if constexpr (decltype(has_prev)::value) {
 #pragma unroll
       for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ch][db], p_prev[ch], acc[db], 0, 0, 0);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ch][db], p_prev[qb][ch], acc[qb][db], 0, 0, 0);
     }
     if constexpr (decltype(has_next)::value) {
-      s_next = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qf[0], f32x16{}, 0, 0, 0);
 #pragma unroll
-      for (int m = 1; m < NM; ++m) s_next = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[m], qf[m], s_next, 0, 0, 0);
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          s_next[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[m], qf[qb][m], m == 0 ? f32x16{} : s_next[qb], 0, 0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (decltype(may_mask)::value) mask_tail(s_next, (t + 1) * BN);
@@ -292,16 +323,19 @@ __device__ __forceinline__ void attend_segment(const AttnArgs& a, uint16_t* ks_b
     __syncthreads();
     gload(vr, vrs, (t + 1) * BN);
     gload(kr, krs, (t + 3) * BN);
-    if constexpr (decltype(has_next)::value) s_cur = s_next;
-    p_prev[0] = pf[0];
-    p_prev[1] = pf[1];
-    // O now holds tiles < t (PV(t-1) was issued above) at the old max: bring it
-    // to the new one before PV(t) is added in the next iteration.
-    if (__ballot(upd)) {
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+    for (int qb = 0; qb < QB; ++qb) {
+      if constexpr (decltype(has_next)::value) s_cur[qb] = s_next[qb];
+      p_prev[qb][0] = pf[qb][0];
+      p_prev[qb][1] = pf[qb][1];
+      // O now holds tiles < t (PV(t-1) was issued above) at the old max: bring it
+      // to the new one before PV(t) is added in the next iteration.
+      if (__ballot(upd[qb])) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[qb][db][r] *= alpha[qb];
+      }
     }
   };
 
@@ -315,41 +349,57 @@ __device__ __forceinline__ void attend_segment(const AttnArgs& a, uint16_t* ks_b
     if (t1 - t0 > 2) iteration(t1 - 2, Flag<true>{}, Flag<true>{}, Flag<true>{});
     iteration(t1 - 1, Flag<true>{}, Flag<false>{}, Flag<false>{});
   }
-  pv(vs((t1 - 1 - t0) & 1), p_prev);
-
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  if (part) {
-    float* pw = part + static_cast<long>(wave) * (NDB * 16 * 64);
+  {
+    const uint16_t* vt = vs((t1 - 1 - t0) & 1);
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) pw[(db * 16 + r) * 64 + lane] = acc[db][r];
-    float* ml = part + attn_waves<HD>() * 64L * NDB * 16;
-    ml[wave * 64 + lane] = m_run;
-    ml[attn_waves<HD>() * 64 + wave * 64 + lane] = l_tot;
-    return;
-  }
-  if (qvalid) {
-    const float inv = 1.0f / l_tot;
-    const long orow = a.out_rows ? static_cast<long>(a.out_rows[qrow]) : qrow;
-    uint16_t* op = a.out + orow * D + head * HD + 4 * hi;
+      for (int db = 0; db < NDB; ++db) {
+        const bf16x8 vfr = v_frag(vt, ch, db);
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const u32x2 val{pack_bf16x2(acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv),
-                        pack_bf16x2(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv)};
-        *reinterpret_cast<u32x2*>(op + db * 32 + g * 8) = val;
+        for (int qb = 0; qb < QB; ++qb)
+          acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr, p_prev[qb][ch], acc[qb][db], 0, 0, 0);
       }
-    if (a.lse && hi == 0) a.lse[head * a.n_q + qrow] = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
+  }
+
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32, 64);
+    const int blk = wave * QB + qb;
+    if (part) {
+      float* pw = part + static_cast<long>(blk) * (NDB * 16 * 64);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pw[(db * 16 + r) * 64 + lane] = acc[qb][db][r];
+      float* ml = part + attn_blocks<HD>() * 64L * NDB * 16;
+      ml[blk * 64 + lane] = m_run[qb];
+      ml[attn_blocks<HD>() * 64 + blk * 64 + lane] = l_tot;
+      continue;
+    }
+    const long qrow = qrow0 + 32 * qb;
+    if (qrow < a.n_q) {
+      const float inv = 1.0f / l_tot;
+      const long orow = a.out_rows ? static_cast<long>(a.out_rows[qrow]) : qrow;
+      uint16_t* op = a.out + orow * D + head * HD + 4 * hi;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const u32x2 val{pack_bf16x2(acc[qb][db][4 * g] * inv, acc[qb][db][4 * g + 1] * inv),
+                          pack_bf16x2(acc[qb][db][4 * g + 2] * inv, acc[qb][db][4 * g + 3] * inv)};
+          *reinterpret_cast<u32x2*>(op + db * 32 + g * 8) = val;
+        }
+      if (a.lse && hi == 0) a.lse[head * a.n_q + qrow] = (m_run[qb] + __log2f(l_tot)) * 0.69314718055994531f;
+    }
   }
 }
 
 template <int HD>
-__global__ __launch_bounds__(64 * attn_waves<HD>(), 2) void attention_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * attn_waves<HD>(), attn_min_blocks<HD>()) void attention_kernel(AttnArgs a) {
   __shared__ __align__(16) uint16_t ks[2 * kAttnBN * (HD + 8)];
   __shared__ __align__(16) uint16_t vs[2 * kAttnBN * (HD + 32)];
-  const long n_qt = (a.n_q + 32 * attn_waves<HD>() - 1) / (32 * attn_waves<HD>());
+  const long n_qt = (a.n_q + attn_rows<HD>() - 1) / attn_rows<HD>();
   const long tile = xcd_remap(blockIdx.x, n_qt * a.heads);
   attend_segment<HD>(a, ks, vs, tile, 0, (a.n_kv + kAttnBN - 1) / kAttnBN, nullptr);
 }
@@ -363,7 +413,7 @@ __global__ __launch_bounds__(64 * attn_waves<HD>(), 2) void attention_kernel(Att
 // and dealt to XCDs in contiguous runs, so the workgroups resident on one XCD
 // at a time read the same key range of the same head and share its L2.
 template <int HD>
-__global__ __launch_bounds__(64 * attn_waves<HD>(), 2) void attention_split_kernel(AttnArgs a, float* ws,
+__global__ __launch_bounds__(64 * attn_waves<HD>(), attn_min_blocks<HD>()) void attention_split_kernel(AttnArgs a, float* ws,
                                                                                    long full, long tail,
                                                                                    int kp) {
   __shared__ __align__(16) uint16_t ks[2 * kAttnBN * (HD + 8)];
@@ -383,10 +433,10 @@ __global__ __launch_bounds__(64 * attn_waves<HD>(), 2) void attention_split_kern
 // One workgroup per cut tile: O = sum_j w_j O_j / sum_j w_j l_j with
 // w_j = 2^(m_j - max_j m_j); bf16 rows (+ LSE) written as attention_kernel does.
 template <int HD>
-__global__ __launch_bounds__(64 * attn_waves<HD>()) void attention_merge_kernel(AttnArgs a, const float* ws,
+__global__ __launch_bounds__(64 * attn_blocks<HD>()) void attention_merge_kernel(AttnArgs a, const float* ws,
                                                                                  long full, int kp) {
   constexpr int NDB = HD / 32;
-  constexpr int NW = attn_waves<HD>();
+  constexpr int NW = attn_blocks<HD>();  // one wave per 32-query block
   constexpr long piece = attn_piece_floats<HD>();
   const long n_qt = (a.n_q + 32 * NW - 1) / (32 * NW);
   const long tile = full + blockIdx.x;
@@ -450,7 +500,7 @@ long resident_ctas() {
 
 template <int HD>
 long query_tiles(long n_q, int heads) {
-  constexpr long bm = 32 * attn_waves<HD>();
+  constexpr long bm = attn_rows<HD>();
   return (n_q + bm - 1) / bm * heads;
 }
 
@@ -514,7 +564,7 @@ hipError_t launch_hd(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t s
                      block, 0, s, a, w, sp.full, sp.tail, sp.kp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attention_merge_kernel<HD>, dim3(static_cast<unsigned>(sp.tail)), block, 0, s, a,
+  hipLaunchKernelGGL(attention_merge_kernel<HD>, dim3(static_cast<unsigned>(sp.tail)), dim3(64 * attn_blocks<HD>()), 0, s, a,
                      static_cast<const float*>(w), sp.full, sp.kp);
   return hipGetLastError();
 }

@@ -25,14 +25,14 @@ namespace tsa {
 
 // ------------------------------------------------------------------ Euler
 
-// x (fp32 or bf16) += dt * v (bf16), 8 elements per thread and iteration.
+// x (fp32 or bf16) += dt * v (bf16), 8 elements per thread.
 // fp32: fmaf rounds the exact value once; bf16: that fp32 result is rounded to
 // nearest even.
 template <typename T>
 __global__ __launch_bounds__(256) void euler_kernel(T* __restrict__ x, const uint16_t* __restrict__ v,
                                                     long n8, float dt) {
-  for (long c = static_cast<long>(blockIdx.x) * 256 + threadIdx.x; c < n8;
-       c += static_cast<long>(gridDim.x) * 256) {
+  const long c = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
+  if (c < n8) {
     float fv[8];
     unpack8(reinterpret_cast<const u32x4*>(v)[c], fv);
     if constexpr (sizeof(T) == 4) {
@@ -60,8 +60,7 @@ __global__ __launch_bounds__(256) void euler_kernel(T* __restrict__ x, const uin
 
 hipError_t launch_euler(void* x, int x_dtype, const uint16_t* v, long n_elems, float dt, hipStream_t s) {
   const long n8 = n_elems / 8;
-  const long blocks = (n8 + 255) / 256;
-  const dim3 grid(static_cast<unsigned>(blocks < 8192 ? blocks : 8192));
+  const dim3 grid(static_cast<unsigned>((n8 + 255) / 256));
   if (x_dtype == kDtypeF32)
     hipLaunchKernelGGL(euler_kernel<float>, grid, dim3(256), 0, s, static_cast<float*>(x), v, n8, dt);
   else
@@ -148,8 +147,8 @@ __global__ __launch_bounds__(kLifThreads) void lif_mask_kernel(const T* __restri
     if (short_out) short_out[loc] = __builtin_inff();
     if (long_out) long_out[loc] = __builtin_inff();
   }
+  if (frames > 1) load_row(cur, 1);
   for (long f = 1; f < frames; ++f) {
-    load_row(cur, f);
     float acc[4] = {0.f, 0.f, 0.f, 0.f};  // short num, short den, long num, long den
 #pragma unroll
     for (int j = 0; j < CPT; ++j)
@@ -160,6 +159,9 @@ __global__ __launch_bounds__(kLifThreads) void lif_mask_kernel(const T* __restri
         acc[2] += fabsf(cur[j][e] - ref[j][e]);
         acc[3] += fabsf(ref[j][e]);
       }
+    // the next frame's row is in flight while this one is reduced
+    float nxt[CPT][V];
+    if (f + 1 < frames) load_row(nxt, f + 1);
     block_sum4(acc, part);
     const float ss = l1_score(acc[0], acc[1], relative);
     const float ls = l1_score(acc[2], acc[3], relative);
@@ -176,6 +178,7 @@ __global__ __launch_bounds__(kLifThreads) void lif_mask_kernel(const T* __restri
       for (int e = 0; e < V; ++e) {
         if (keep) ref[j][e] = cur[j][e];
         prev[j][e] = cur[j][e];
+        if (f + 1 < frames) cur[j][e] = nxt[j][e];
       }
   }
 }
@@ -208,20 +211,33 @@ hipError_t launch_lif_mask(const void* x, int dtype, long frames, long hw, long 
 
 // ----------------------------------------------------------- restoration
 
-// Thread = (location, 16-byte slice); rows of row_bytes bytes.
+// Thread = (location, 16-byte slice); rows of row_bytes bytes.  The kept
+// slices of up to 8 frames are loaded together, then the pruned ones written.
 __global__ __launch_bounds__(256) void restore_kernel(u32x4* __restrict__ buf, const uint8_t* __restrict__ mask,
                                                       long frames, long hw, long slices) {
+  constexpr int kF = 8;
   const long id = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
   if (id >= hw * slices) return;
   const long loc = id / slices, sl = id - loc * slices;
   u32x4 carry = buf[loc * slices + sl];
-  for (long f = 1; f < frames; ++f) {
-    const long t = f * hw + loc;
-    u32x4* p = buf + t * slices + sl;
-    if (mask[t])
-      carry = *p;
-    else
-      *p = carry;
+  for (long f0 = 1; f0 < frames; f0 += kF) {
+    bool kept[kF];
+    u32x4 r[kF];
+#pragma unroll
+    for (int i = 0; i < kF; ++i) {
+      const long f = f0 + i;
+      kept[i] = f < frames && mask[f * hw + loc];
+      if (kept[i]) r[i] = buf[(f * hw + loc) * slices + sl];
+    }
+#pragma unroll
+    for (int i = 0; i < kF; ++i) {
+      const long f = f0 + i;
+      if (f >= frames) break;
+      if (kept[i])
+        carry = r[i];
+      else
+        buf[(f * hw + loc) * slices + sl] = carry;
+    }
   }
 }
 

@@ -39,8 +39,10 @@ struct RowLoad<float> {  // fp32: 4 elements per 16-byte load
 };
 
 // One wave per token row: each lane accumulates sum|x - r| and sum|r| over
-// its 16-byte slices, then a butterfly reduction.  Fixed order: deterministic.
-template <typename T>
+// its 16-byte slices, then a butterfly reduction.  The slices of a lane are
+// loaded in batches of B, all loads of a batch issued before any is used, so a
+// wave keeps 2*B 16-byte loads in flight.  Fixed order: deterministic.
+template <typename T, int B>
 __global__ __launch_bounds__(256) void score_kernel(const T* __restrict__ x_cur,
                                                     const T* __restrict__ ref,
                                                     long ref_off, long n_rows, long dim,
@@ -54,18 +56,28 @@ __global__ __launch_bounds__(256) void score_kernel(const T* __restrict__ x_cur,
     if (lane == 0) scores[row] = __builtin_inff();
     return;
   }
-  const T* a = x_cur + row * dim;
-  const T* b = ref + rr * dim;
+  const u32x4* a = reinterpret_cast<const u32x4*>(x_cur + row * dim);
+  const u32x4* b = reinterpret_cast<const u32x4*>(ref + rr * dim);
+  const long nsl = dim / V;
   float num = 0.f, den = 0.f;
-#pragma unroll 4
-  for (long c = static_cast<long>(lane) * V; c < dim; c += 64 * V) {
-    float fa[V], fb[V];
-    RowLoad<T>::load(a + c, fa);
-    RowLoad<T>::load(b + c, fb);
+  for (long c0 = 0; c0 < nsl; c0 += 64 * B) {
+    u32x4 ra[B], rb[B];
 #pragma unroll
-    for (int i = 0; i < V; ++i) {
-      num += fabsf(fa[i] - fb[i]);
-      den += fabsf(fb[i]);
+    for (int j = 0; j < B; ++j) {
+      const long c = c0 + lane + 64 * j;
+      ra[j] = c < nsl ? a[c] : u32x4{0u, 0u, 0u, 0u};
+      rb[j] = c < nsl ? b[c] : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      float fa[V], fb[V];
+      RowLoad<T>::load(reinterpret_cast<const T*>(&ra[j]), fa);
+      RowLoad<T>::load(reinterpret_cast<const T*>(&rb[j]), fb);
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        num += fabsf(fa[i] - fb[i]);
+        den += fabsf(fb[i]);
+      }
     }
   }
   num = wave_sum(num);
@@ -325,19 +337,28 @@ __global__ void map_groups_kernel(const uint8_t* __restrict__ group, int n, Grou
 
 // ------------------------------------------------------------------ launch
 
+template <typename T, int B>
+void launch_scores_t(const void* x_cur, const void* x_ref, long ref_off, long n_rows, long dim,
+                     int relative, float* scores, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((n_rows + 3) / 4));
+  hipLaunchKernelGGL((score_kernel<T, B>), grid, dim3(256), 0, s, static_cast<const T*>(x_cur),
+                     static_cast<const T*>(x_ref ? x_ref : x_cur), ref_off, n_rows, dim, relative, scores);
+}
+
 hipError_t launch_scores(const void* x_cur, const void* x_ref, long ref_off, long n_rows,
                          long dim, int dtype, int relative, float* scores, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>((n_rows + 3) / 4));
+  // slices per lane: a batch large enough for the whole row up to 64*4 slices
+  const long per_lane = (dim / (dtype == kDtypeBf16 ? 8 : 4) + 63) / 64;
   if (dtype == kDtypeBf16) {
-    hipLaunchKernelGGL(score_kernel<uint16_t>, grid, dim3(256), 0, s,
-                       static_cast<const uint16_t*>(x_cur),
-                       static_cast<const uint16_t*>(x_ref ? x_ref : x_cur), ref_off, n_rows, dim,
-                       relative, scores);
+    if (per_lane <= 2)
+      launch_scores_t<uint16_t, 2>(x_cur, x_ref, ref_off, n_rows, dim, relative, scores, s);
+    else
+      launch_scores_t<uint16_t, 4>(x_cur, x_ref, ref_off, n_rows, dim, relative, scores, s);
   } else {
-    hipLaunchKernelGGL(score_kernel<float>, grid, dim3(256), 0, s,
-                       static_cast<const float*>(x_cur),
-                       static_cast<const float*>(x_ref ? x_ref : x_cur), ref_off, n_rows, dim,
-                       relative, scores);
+    if (per_lane <= 2)
+      launch_scores_t<float, 2>(x_cur, x_ref, ref_off, n_rows, dim, relative, scores, s);
+    else
+      launch_scores_t<float, 4>(x_cur, x_ref, ref_off, n_rows, dim, relative, scores, s);
   }
   return hipGetLastError();
 }
