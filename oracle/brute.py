@@ -196,3 +196,46 @@ def restore(buf, mask, frames, hw):
                     src -= 1
                 out[t] = list(buf[src * hw + loc])  # a kept frame, or frame 0
     return out
+
+
+def rope(x_rows, tokens, height, width, heads, base=10000.0):
+    """Rotate each adjacent channel pair of every head by its axis position times the pair's
+    frequency; time / height / width channel groups of sizes d - 4*(d//6), 2*(d//6), 2*(d//6)."""
+    dim = len(x_rows[0])
+    d = dim // heads
+    g = 2 * (d // 6)
+    groups = [(0, d - 2 * g, 0), (d - 2 * g, g, 1), (d - g, g, 2)]
+    out = []
+    for row, t in zip(x_rows, tokens):
+        pos = (t // (height * width), (t // width) % height, t % width)
+        r = list(row)
+        for h in range(heads):
+            for start, size, axis in groups:
+                for i in range(size // 2):
+                    theta = pos[axis] * base ** (-2.0 * i / size)
+                    j = h * d + start + 2 * i
+                    a, b = row[j], row[j + 1]
+                    r[j] = a * math.cos(theta) - b * math.sin(theta)
+                    r[j + 1] = a * math.sin(theta) + b * math.cos(theta)
+        out.append(r)
+    return out
+
+
+def attention_frame_causal(q, k, v, heads, q_tokens, frame_tokens, scale=None):
+    """Query of token t sees keys j with j // frame_tokens <= t // frame_tokens."""
+    dim = len(q[0])
+    d = dim // heads
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = [[0.0] * dim for _ in q]
+    for i, (qi, t) in enumerate(zip(q, q_tokens)):
+        keys = [j for j in range(len(k)) if j // frame_tokens <= t // frame_tokens]
+        for h in range(heads):
+            c0 = h * d
+            s = [scale * math.fsum(qi[c0 + u] * k[j][c0 + u] for u in range(d)) for j in keys]
+            mx = max(s)
+            p = [math.exp(x - mx) for x in s]
+            z = math.fsum(p)
+            for u in range(d):
+                out[i][c0 + u] = math.fsum(pj * v[j][c0 + u] for pj, j in zip(p, keys)) / z
+    return out

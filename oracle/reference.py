@@ -234,12 +234,15 @@ def init_kv_cache(x, w_qkv) -> tuple[np.ndarray, np.ndarray]:
 
 def layer_step(x_cur, w_qkv, heads: int, k_cache, v_cache, out, *, mask=None, x_ref=None,
                ref_row_offset: int = 0, k: int | None = None, tau: float | None = None,
-               relative: bool = True) -> dict:
+               relative: bool = True, rope=None, causal_frame_tokens: int | None = None) -> dict:
     """One pruned layer step (HSA page §2.2): score, select, compact, project the active
     tokens, sync their K/V into the cache, attend, scatter.  Updates the cache and ``out``
     in place and returns the intermediate results.
 
     Selection: ``mask`` if given, else top-``k`` if ``k`` is given, else ``s >= tau``.
+    Variants: ``rope = (height, width, base)`` rotates Q and K by their tokens' 3D
+    positions before storage (project_rope); ``causal_frame_tokens`` restricts every query
+    to the keys of frames up to its own (attention_frame_causal).
     """
     scores = None
     if mask is None:
@@ -250,9 +253,16 @@ def layer_step(x_cur, w_qkv, heads: int, k_cache, v_cache, out, *, mask=None, x_
     if idx.size == 0:
         res["o_a"] = np.zeros((0, out.shape[1]))
         return res
-    p = project(np.asarray(x_cur, dtype=np.float64)[idx], w_qkv, "qkv")
+    xa = np.asarray(x_cur, dtype=np.float64)[idx]
+    if rope is None:
+        p = project(xa, w_qkv, "qkv")
+    else:
+        p = project_rope(xa, idx, w_qkv, heads, *rope, parts="qkv")
     kv_cache_sync(k_cache, v_cache, idx, p["k"], p["v"])
-    o_a = attention(p["q"], k_cache, v_cache, heads)
+    if causal_frame_tokens is None:
+        o_a = attention(p["q"], k_cache, v_cache, heads)
+    else:
+        o_a = attention_frame_causal(p["q"], k_cache, v_cache, heads, idx, causal_frame_tokens)
     scatter(out, idx, o_a)
     res.update(q=p["q"], k=p["k"], v=p["v"], o_a=o_a)
     return res
@@ -417,3 +427,86 @@ def restore_frames(buf, mask, frames: int, hw: int) -> np.ndarray:
         pruned = ~m[f]
         b[f, pruned] = b[f - 1, pruned]
     return b.reshape(frames * hw, -1)
+
+
+# ------------------------------------- f3: 3D rotary positions, frame-causal attention
+
+def rope_split(head_dim: int) -> tuple:
+    """Channels of one head given to the time, height and width axes: the two spatial axes
+    take 2 * floor(d / 6) each and the time axis the rest (d = 128: 44 / 42 / 42)."""
+    s = 2 * (head_dim // 6)
+    return head_dim - 2 * s, s, s
+
+
+def token_position(tokens, height: int, width: int) -> tuple:
+    """(frame, row, column) of frame-major token indices."""
+    t = np.asarray(tokens, dtype=np.int64)
+    return t // (height * width), (t // width) % height, t % width
+
+
+def rope3d(x_rows, tokens, height: int, width: int, heads: int, base: float = 10000.0) -> np.ndarray:
+    """Rotary position embedding over the three latent axes.  The Timeripple page
+    (Metodología, §1, structured encoding) describes the RoPE of video DiTs as splitting a
+    head's channels into a temporal group and two spatial groups (x and y); LIPAR page §2.C
+    requires the pruned path to respect those rotations.  Q and K are rotated by their own
+    tokens' positions.  Each head's channels are split into time / height / width groups
+    (rope_split, the group sizes being this build's reading); inside the group of axis a,
+    of size d_a, the channel pair
+    (2i, 2i+1), read as the complex number x_2i + i x_2i+1, is multiplied by
+    exp(i p_a base^(-2i/d_a)), p_a being the token's coordinate along a.  Float64, not rounded.
+    """
+    x = np.asarray(x_rows, dtype=np.float64)
+    dim = x.shape[1]
+    d = dim // heads
+    d_t, d_y, d_x = rope_split(d)
+    f, y, xx = token_position(tokens, height, width)
+    out = x.copy()
+    for h in range(heads):
+        for off, d_a, pos in ((0, d_t, f), (d_t, d_y, y), (d_t + d_y, d_x, xx)):
+            i = np.arange(d_a // 2)
+            ang = pos[:, None].astype(np.float64) * (float(base) ** (-2.0 * i / d_a))[None, :]
+            c, s = np.cos(ang), np.sin(ang)
+            ev = h * d + off + 2 * i
+            a, b = x[:, ev], x[:, ev + 1]
+            out[:, ev] = a * c - b * s
+            out[:, ev + 1] = a * s + b * c
+    return out
+
+
+def project_rope(x_rows, tokens, w_qkv, heads: int, height: int, width: int, base: float = 10000.0,
+                 parts: str = "qkv") -> dict:
+    """project() with Q and K rotated (rope3d) by the positions of their tokens before they are
+    stored: the exact projection is rotated, then rounded to bf16 once.  V is not rotated."""
+    x = round_bf16(np.asarray(x_rows, dtype=np.float64))
+    w = np.asarray(w_qkv, dtype=np.float64)
+    d = w.shape[1]
+    out = {}
+    for i, name in enumerate("qkv"):
+        if name in parts:
+            y = x @ w[i * d:(i + 1) * d].T
+            if name in "qk":
+                y = rope3d(y, tokens, height, width, heads, base)
+            out[name] = round_bf16(y)
+    return out
+
+
+def attention_frame_causal(q, k, v, heads: int, q_tokens, frame_tokens: int, scale: float | None = None,
+                           return_lse: bool = False):
+    """Frame-causal variant of attention() for causal video models (LIPAR page §3 and §4: the
+    method serves causal models such as Self-Forcing as well as bidirectional ones): the
+    query of token t sees only the keys of the frames up to its own,
+    j < (t // frame_tokens + 1) * frame_tokens (a block-causal mask, one block per frame).  Queries of one frame share a key range, so each group is
+    plain attention() over that prefix of the cache."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    frames = np.asarray(q_tokens, dtype=np.int64) // frame_tokens
+    out = np.zeros_like(q)
+    lse = np.zeros((heads, q.shape[0]))
+    for f in np.unique(frames):
+        rows = np.flatnonzero(frames == f)
+        lim = min(k.shape[0], (int(f) + 1) * frame_tokens)
+        o, l = attention(q[rows], k[:lim], v[:lim], heads, scale, return_lse=True)
+        out[rows] = o
+        lse[:, rows] = l
+    return (out, lse) if return_lse else out

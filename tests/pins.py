@@ -340,3 +340,91 @@ def check_restore(restore_frames):
     got = restore_frames(buf, mask, frames, hw)
     assert np.array_equal(got[mask], buf[mask])
     assert np.array_equal(got, np.array(brute.restore(buf.tolist(), mask.tolist(), frames, hw)))
+
+
+# ------------------------------------ f3: 3D rotary positions, frame-causal attention
+
+def check_rope(rope3d, rope_split, token_position):
+    assert rope_split(128) == (44, 42, 42) and rope_split(64) == (24, 20, 20)
+    h, w = 3, 5
+    f, y, x = token_position(np.array([0, 4, 5, 14, 15, 37]), h, w)
+    assert list(f) == [0, 0, 0, 0, 1, 2] and list(y) == [0, 0, 1, 2, 0, 1] and list(x) == [0, 4, 0, 4, 0, 2]
+    r = rng(16)
+    heads, d = 2, 24
+    dt, dy, dx = rope_split(d)
+    xrows = r.standard_normal((6, heads * d))
+    toks = np.array([0, 7, 15, 16, 44, 59])
+    # token 0 sits at the origin: no rotation
+    assert np.array_equal(rope3d(xrows[:1], [0], h, w, heads), xrows[:1])
+    # closed form: a unit vector on pair i of the width group of head 1, token at column 1
+    for i in range(dx // 2):
+        e = np.zeros((1, heads * d))
+        e[0, d + dt + dy + 2 * i] = 1.0
+        got = rope3d(e, [1], h, w, heads, base=100.0)
+        phi = 100.0 ** (-2.0 * i / dx)
+        want = np.zeros_like(e)
+        want[0, d + dt + dy + 2 * i] = np.cos(phi)
+        want[0, d + dt + dy + 2 * i + 1] = np.sin(phi)
+        assert np.allclose(got, want, rtol=0, atol=1e-15)
+    # closed form: pair 0 of the time group turns by the frame index (frequency 1)
+    e = np.zeros((1, heads * d))
+    e[0, 0] = 1.0
+    got = rope3d(e, [2 * h * w], h, w, heads)
+    assert np.allclose(got[0, :2], [np.cos(2.0), np.sin(2.0)], rtol=0, atol=1e-15)
+    # rotations: every channel pair keeps its length
+    out = rope3d(xrows, toks, h, w, heads)
+    assert np.allclose(out[:, 0::2] ** 2 + out[:, 1::2] ** 2, xrows[:, 0::2] ** 2 + xrows[:, 1::2] ** 2,
+                       rtol=1e-13, atol=0)
+    # scores depend only on the offset between the two positions (shift both along each axis)
+    q, k = r.standard_normal((1, heads * d)), r.standard_normal((1, heads * d))
+    for a, b, shift in ((3, 8, 1), (0, 16, 15), (6, 21, 5)):  # column, row (w), frame (h*w) shifts
+        s0 = rope3d(q, [a], h, w, heads) @ rope3d(k, [b], h, w, heads).T
+        s1 = rope3d(q, [a + shift], h, w, heads) @ rope3d(k, [b + shift], h, w, heads).T
+        assert np.allclose(s0, s1, rtol=1e-12, atol=1e-12)
+    # brute force
+    assert np.allclose(out, np.array(brute.rope(xrows.tolist(), toks.tolist(), h, w, heads)), rtol=1e-13, atol=1e-13)
+
+
+def check_project_rope(project_rope, project, rope3d):
+    r = rng(17)
+    heads, d = 2, 24
+    x = bf16_values(r.standard_normal((5, heads * d)))
+    w = bf16_values(r.standard_normal((3 * heads * d, heads * d)) / np.sqrt(heads * d))
+    toks = np.array([0, 3, 19, 20, 41])
+    p = project_rope(x, toks, w, heads, 4, 5)
+    plain = project(x, w, "qkv")
+    # V is not rotated; a token at the origin is not rotated at all
+    assert np.array_equal(p["v"], plain["v"])
+    assert np.array_equal(p["q"][0], plain["q"][0]) and np.array_equal(p["k"][0], plain["k"][0])
+    # rotation of the exact projection, rounded once
+    for name, part in (("q", 0), ("k", 1)):
+        exact = x.astype(np.float64) @ w[part * heads * d:(part + 1) * heads * d].T
+        want = rope3d(exact, toks, 4, 5, heads)
+        assert np.allclose(p[name], want, rtol=2.0 ** -8, atol=1e-12)
+        assert np.array_equal(p[name], bf16_values(want))
+
+
+def check_frame_causal(attention_frame_causal, attention):
+    r = rng(18)
+    heads, d, ft = 2, 8, 6
+    n_kv = 27
+    k = r.standard_normal((n_kv, heads * d))
+    v = r.standard_normal((n_kv, heads * d))
+    toks = np.array([0, 2, 5, 6, 11, 13, 20, 26])
+    q = r.standard_normal((toks.size, heads * d))
+    out = attention_frame_causal(q, k, v, heads, toks, ft)
+    # one frame covering the whole cache: plain attention
+    assert np.allclose(attention_frame_causal(q, k, v, heads, toks, n_kv + 5), attention(q, k, v, heads),
+                       rtol=1e-14, atol=1e-14)
+    # a frame-0 query equals attention over the first frame's keys only; the last frame sees all
+    assert np.allclose(out[:3], attention(q[:3], k[:ft], v[:ft], heads), rtol=1e-14, atol=1e-14)
+    assert np.allclose(out[-1:], attention(q[-1:], k, v, heads), rtol=1e-14, atol=1e-14)
+    # keys of later frames do not matter (change them arbitrarily)
+    k2, v2 = k.copy(), v.copy()
+    k2[12:] = r.standard_normal(k2[12:].shape) * 5
+    v2[12:] = r.standard_normal(v2[12:].shape) * 5
+    mid = toks < 12
+    assert np.allclose(attention_frame_causal(q[mid], k2, v2, heads, toks[mid], ft), out[mid], rtol=1e-14, atol=1e-14)
+    # brute force
+    want = brute.attention_frame_causal(q.tolist(), k.tolist(), v.tolist(), heads, toks.tolist(), ft)
+    assert np.allclose(out, np.array(want), rtol=1e-12, atol=1e-12)

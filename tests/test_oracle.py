@@ -248,3 +248,45 @@ def test_lif_mask_pinned():
 
 def test_restore_pinned():
     pins.check_restore(ref.restore_frames)
+
+
+# -------------------------------------------- f3: rotary positions, frame-causal attention
+
+def test_rope_pinned():
+    pins.check_rope(ref.rope3d, ref.rope_split, ref.token_position)
+
+
+def test_project_rope_pinned():
+    pins.check_project_rope(ref.project_rope, ref.project, ref.rope3d)
+
+
+def test_frame_causal_pinned():
+    pins.check_frame_causal(ref.attention_frame_causal, ref.attention)
+
+
+def test_layer_step_rope_causal_matches_brute_force():
+    r = np.random.default_rng(19)
+    n, dim, heads, h, w = 24, 16, 2, 2, 3
+    x = pins.bf16_values(r.standard_normal((n, dim)))
+    w_qkv = pins.bf16_values(r.standard_normal((3 * dim, dim)) / np.sqrt(dim))
+    mask = r.random(n) < 0.5
+    mask[[0, n - 1]] = True
+    kc, vc = ref.init_kv_cache(x, w_qkv)
+    out = np.zeros((n, dim))
+    res = ref.layer_step(x, w_qkv, heads, kc, vc, out, mask=mask, rope=(h, w, 10000.0),
+                         causal_frame_tokens=h * w)
+    idx = res["idx"]
+    # brute force: exact projections, rotated, rounded; cache rows replaced; causal attention
+    xb = [[brute.bf16(v) for v in row] for row in x[idx].tolist()]
+    exact = {p: brute.matmul_t(xb, w_qkv[i * dim:(i + 1) * dim].tolist()) for i, p in enumerate("qkv")}
+    rq = [[brute.bf16(v) for v in row] for row in brute.rope(exact["q"], idx.tolist(), h, w, heads)]
+    rk = [[brute.bf16(v) for v in row] for row in brute.rope(exact["k"], idx.tolist(), h, w, heads)]
+    rv = [[brute.bf16(v) for v in row] for row in exact["v"]]
+    kb, vb = ref.init_kv_cache(x, w_qkv)
+    kb, vb = kb.tolist(), vb.tolist()
+    for j, t in enumerate(idx):
+        kb[t], vb[t] = rk[j], rv[j]
+    o = brute.attention_frame_causal(rq, kb, vb, heads, idx.tolist(), h * w)
+    assert np.array_equal(res["q"], np.array(rq))
+    assert np.allclose(kc, np.array(kb), rtol=0, atol=0)
+    assert np.allclose(res["o_a"], np.array(o), rtol=1e-12, atol=1e-12)

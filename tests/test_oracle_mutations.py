@@ -247,3 +247,56 @@ def _restore_from_original(buf, mask, frames, hw):
 
 def test_restore_mutation_caught():
     _fails(pins.check_restore, _restore_from_original)
+
+
+# ------------------------------------ f3: rotary positions, frame-causal attention
+
+def _rope_generic(x_rows, tokens, height, width, heads, base=10000.0, sign=1.0, halves=False, swap_xy=False):
+    x = np.asarray(x_rows, dtype=np.float64)
+    d = x.shape[1] // heads
+    d_t, d_y, d_x = ref.rope_split(d)
+    f, y, xx = ref.token_position(tokens, height, width)
+    if swap_xy:
+        y, xx = xx, y
+    out = x.copy()
+    for h in range(heads):
+        for off, d_a, pos in ((0, d_t, f), (d_t, d_y, y), (d_t + d_y, d_x, xx)):
+            i = np.arange(d_a // 2)
+            ang = pos[:, None] * (base ** (-2.0 * i / d_a))[None, :]
+            c, s = np.cos(ang), sign * np.sin(ang)
+            ev = h * d + off + (i if halves else 2 * i)
+            od = ev + (d_a // 2 if halves else 1)
+            a, b = x[:, ev], x[:, od]
+            out[:, ev] = a * c - b * s
+            out[:, od] = a * s + b * c
+    return out
+
+
+@pytest.mark.parametrize("kw", [{"sign": -1.0}, {"halves": True}, {"swap_xy": True}])
+def test_rope_mutations_caught(kw):
+    _fails(pins.check_rope, lambda *a, **k: _rope_generic(*a, **{**k, **kw}), ref.rope_split, ref.token_position)
+
+
+def test_project_rope_mutation_caught():
+    def rotate_after_rounding(x_rows, tokens, w_qkv, heads, height, width, base=10000.0, parts="qkv"):
+        p = ref.project(x_rows, w_qkv, parts)
+        return {n: (ref.round_bf16(ref.rope3d(p[n], tokens, height, width, heads, base)) if n in "qk" else p[n])
+                for n in p}
+    _fails(pins.check_project_rope, rotate_after_rounding, ref.project, ref.rope3d)
+
+
+def _causal_shifted(shift):
+    def run(q, k, v, heads, q_tokens, frame_tokens, scale=None, return_lse=False):
+        frames = np.asarray(q_tokens) // frame_tokens
+        out = np.zeros_like(np.asarray(q, np.float64))
+        for f in np.unique(frames):
+            rows = np.flatnonzero(frames == f)
+            lim = max(1, min(len(k), (int(f) + 1 + shift) * frame_tokens))
+            out[rows] = ref.attention(np.asarray(q)[rows], np.asarray(k)[:lim], np.asarray(v)[:lim], heads, scale)
+        return out
+    return run
+
+
+@pytest.mark.parametrize("shift", [1, -1])
+def test_frame_causal_mutations_caught(shift):
+    _fails(pins.check_frame_causal, _causal_shifted(shift), ref.attention)
