@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define TSA_ABI_VERSION 3
+#define TSA_ABI_VERSION 4
 
 typedef uint16_t tsa_bf16;
 
@@ -175,6 +175,27 @@ tsa_status tsa_qkv_active(const void* x, int x_dtype, int64_t n_x_rows, const in
                           void* stream);
 
 /*
+ * tsa_qkv_active with 3D rotary positions on Q and K (the RoPE of video DiTs:
+ * [Timeripple] Metodología §1 describes its channels split into a temporal
+ * group and two spatial groups; [LIPAR] §2.C).  Token t sits at frame
+ * t / (height*width), row (t / width) % height, column t % width.  Each
+ * head's head_dim = dim / heads channels are split into time / height / width
+ * groups of head_dim - 4*(head_dim/6), 2*(head_dim/6), 2*(head_dim/6)
+ * channels; inside the group of an axis of size n, channel pair (2i, 2i+1)
+ * is rotated by the angle pos * rope_base^(-2i/n) (pos = the token's
+ * coordinate on that axis), in fp32 on the fp32 product, before the single
+ * bf16 rounding.  V is not rotated; the cache therefore holds rotated K.
+ * Arguments as tsa_qkv_active, plus heads (head_dim even, >= 6), height,
+ * width >= 1 and rope_base > 0 (finite).
+ * Errors: INVALID_ARG, SHAPE, DTYPE, ALIGNMENT, HIP.
+ */
+tsa_status tsa_qkv_active_rope(const void* x, int x_dtype, int64_t n_x_rows, const int32_t* rows,
+                               int64_t n, int64_t dim, const tsa_bf16* w_qkv, tsa_bf16* q_out,
+                               tsa_bf16* k_out, tsa_bf16* v_out, int out_is_cache, int64_t n_cache,
+                               const tsa_bf16* eps, int64_t src_row_offset, float sigma, int heads,
+                               int64_t height, int64_t width, float rope_base, void* stream);
+
+/*
  * a6: [HSA] §2.2 item 2 -- the fresh K/V of the active tokens overwrite
  * their rows of the per-layer cache; every other row keeps its stale entry.
  *   k_a, v_a          device bf16 [n, dim] (compact, row r belongs to token rows[r]).
@@ -221,6 +242,23 @@ tsa_status tsa_sparse_query_attention(const tsa_bf16* q, const tsa_bf16* k_cache
                                       int heads, int head_dim, float scale, tsa_bf16* out,
                                       const int32_t* out_rows, int64_t n_out, float* lse_out,
                                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Frame-causal variant of tsa_sparse_query_attention (causal video models:
+ * [LIPAR] §3-§4, causal Self-Forcing as well as bidirectional models): the
+ * query of token t = q_tokens[r] attends only to the keys of the frames up to
+ * its own, j < (t / frame_tokens + 1) * frame_tokens (capped at n_kv); a
+ * block-causal mask with one block per frame of frame_tokens tokens.  Every
+ * query sees at least key 0.  Same arguments, layouts and rounding as
+ * tsa_sparse_query_attention otherwise (no split schedule).
+ *   q_tokens     device i32[n_q], token index of each query row, >= 0.
+ *   frame_tokens tokens per frame (H*W), >= 1.
+ * Errors: INVALID_ARG, SHAPE, ALIGNMENT, HIP.
+ */
+tsa_status tsa_frame_causal_attention(const tsa_bf16* q, const tsa_bf16* k_cache, const tsa_bf16* v_cache,
+                                      int64_t n_q, int64_t n_kv, int heads, int head_dim, float scale,
+                                      const int32_t* q_tokens, int64_t frame_tokens, tsa_bf16* out,
+                                      const int32_t* out_rows, int64_t n_out, float* lse_out, void* stream);
 
 /*
  * Workspace size for tsa_sparse_query_attention on the current device (the

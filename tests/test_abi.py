@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(root):
 
 
 def test_version_and_status_strings():
-    assert tsa.abi_version() == 3
+    assert tsa.abi_version() == 4
     assert tsa.status_string(0) == "ok"
     assert "shape" in tsa.status_string(B.ERR_SHAPE)
     assert tsa.status_string(99) == "unknown status"
@@ -171,3 +171,36 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "_lib_handle", None)
     with pytest.raises(ImportError):
         B.lib()
+
+
+def test_rope_and_causal_validation():
+    f = lib()
+
+    def qr(**kw):
+        a = dict(x=A, dt=B.BF16, nx=64, rows=None, n=16, dim=128, w=A, q=A, k=A, v=A, cache=0, nc=0,
+                 eps=None, off=0, sigma=0.0, heads=2, h=4, w_=4, base=10000.0)
+        a.update(kw)
+        return f.tsa_qkv_active_rope(a["x"], a["dt"], a["nx"], a["rows"], a["n"], a["dim"], a["w"], a["q"],
+                                     a["k"], a["v"], a["cache"], a["nc"], a["eps"], a["off"], a["sigma"],
+                                     a["heads"], a["h"], a["w_"], a["base"], None)
+    assert qr(n=0) == B.OK
+    assert qr(heads=3) == B.ERR_SHAPE       # 128 / 3 not an integer head dim
+    assert qr(heads=64) == B.ERR_SHAPE      # head dim 2 < 6
+    assert qr(h=0) == B.ERR_SHAPE
+    assert qr(base=0.0) == B.ERR_INVALID_ARG
+    assert qr(base=float("inf")) == B.ERR_INVALID_ARG
+    assert qr(x=None) == B.ERR_INVALID_ARG
+    assert qr(w=U) == B.ERR_ALIGNMENT
+
+    def fc(**kw):
+        a = dict(q=A, k=A, v=A, nq=16, nkv=64, heads=2, hd=64, scale=0.0, qt=A, ft=8, out=A, rows=None, nout=0,
+                 lse=None)
+        a.update(kw)
+        return f.tsa_frame_causal_attention(a["q"], a["k"], a["v"], a["nq"], a["nkv"], a["heads"], a["hd"],
+                                            a["scale"], a["qt"], a["ft"], a["out"], a["rows"], a["nout"],
+                                            a["lse"], None)
+    assert fc(nq=0) == B.OK
+    assert fc(qt=None) == B.ERR_INVALID_ARG
+    assert fc(ft=0) == B.ERR_SHAPE
+    assert fc(hd=96) == B.ERR_SHAPE
+    assert fc(qt=A + 2) == B.ERR_ALIGNMENT

@@ -21,12 +21,14 @@ from ._binding import (
     assign_groups,
     attention_workspace_bytes,
     euler_update,
+    frame_causal_attention,
     gather_rows,
     kv_cache_sync,
     lif_mask,
     lib,
     lib_path,
     qkv_active,
+    qkv_active_rope,
     restore_frames,
     scatter_out,
     select_active,
@@ -41,8 +43,8 @@ lib()  # load now: fail loudly when the HIP library is missing
 
 __all__ = [
     "BF16", "F32", "SCORE_ABS_L1", "SCORE_REL_L1", "SELECT_MASK", "SELECT_SCHEDULE",
-    "SELECT_THRESHOLD", "SELECT_TOPK", "TsaError", "abi_version", "assign_groups", "attention_workspace_bytes", "euler_update", "gather_rows",
-    "kv_cache_sync", "lib", "lib_path", "lif_mask", "qkv_active", "restore_frames", "scatter_out", "select_active",
+    "SELECT_THRESHOLD", "SELECT_TOPK", "TsaError", "abi_version", "assign_groups", "attention_workspace_bytes", "euler_update", "frame_causal_attention", "gather_rows",
+    "kv_cache_sync", "lib", "lib_path", "lif_mask", "qkv_active", "qkv_active_rope", "restore_frames", "scatter_out", "select_active",
     "select_workspace_bytes", "sparse_query_attention", "status_string", "token_scores",
     "PrunedAttentionLayer", "hsa_active_count",
 ]

@@ -44,6 +44,10 @@ _SIGNATURES = {
     "tsa_attention_workspace_bytes": (_size, [_i64, _i64, _int, _int]),
     "tsa_scatter_out": (_int, [_vp, _vp, _i64, _vp, _i64, _i64, _vp]),
     "tsa_gather_rows": (_int, [_vp, _i64, _vp, _i64, _i64, _vp, _i64, _f32, _vp, _vp]),
+    "tsa_qkv_active_rope": (_int, [_vp, _int, _i64, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _int, _i64,
+                                   _vp, _i64, _f32, _int, _i64, _i64, _f32, _vp]),
+    "tsa_frame_causal_attention": (_int, [_vp, _vp, _vp, _i64, _i64, _int, _int, _f32, _vp, _i64, _vp, _vp,
+                                          _i64, _vp, _vp]),
     "tsa_token_scores": (_int, [_vp, _vp, _i64, _i64, _i64, _int, _int, _vp, _vp]),
     "tsa_euler_update": (_int, [_vp, _int, _vp, _i64, _i64, _f32, _vp]),
     "tsa_lif_mask": (_int, [_vp, _int, _i64, _i64, _i64, _int, _f32, _f32, _vp, _vp, _vp, _vp]),
@@ -246,3 +250,24 @@ def token_scores(x_cur, x_ref, scores_out, *, ref_row_offset=0, score_kind=SCORE
                                 int(x_cur.shape[1]), _dtype_code(x_cur), int(score_kind), _ptr(scores_out),
                                 _stream(stream))
     _check("tsa_token_scores", st)
+
+
+def qkv_active_rope(x, rows, n, w_qkv, heads, height, width, *, rope_base=10000.0, q_out=None, k_out, v_out,
+                    out_is_cache=False, n_cache=0, eps=None, src_row_offset=0, sigma=0.0, stream=None):
+    """qkv_active with 3D rotary positions on Q and K (tsa_qkv_active_rope)."""
+    st = lib().tsa_qkv_active_rope(
+        _ptr(x), _dtype_code(x), int(x.shape[0]), _ptr(rows), int(n), int(x.shape[1]), _ptr(w_qkv),
+        _ptr(q_out), _ptr(k_out), _ptr(v_out), 1 if out_is_cache else 0, int(n_cache), _ptr(eps),
+        int(src_row_offset), float(sigma), int(heads), int(height), int(width), float(rope_base),
+        _stream(stream))
+    _check("tsa_qkv_active_rope", st)
+
+
+def frame_causal_attention(q, k_cache, v_cache, n_q, heads, head_dim, q_tokens, frame_tokens, out, *,
+                           out_rows=None, scale=0.0, lse_out=None, stream=None):
+    """Frame-causal attention of the active queries (tsa_frame_causal_attention)."""
+    st = lib().tsa_frame_causal_attention(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), int(n_q), int(k_cache.shape[0]), int(heads), int(head_dim),
+        float(scale), _ptr(q_tokens), int(frame_tokens), _ptr(out), _ptr(out_rows), int(out.shape[0]),
+        _ptr(lse_out), _stream(stream))
+    _check("tsa_frame_causal_attention", st)

@@ -69,6 +69,10 @@ struct AttnArgs {
   uint16_t* out;
   const int* out_rows;
   float* lse;
+  // frame-causal variant: query r is token q_tokens[r] and sees the keys of the frames up
+  // to its own, j < (q_tokens[r] / frame_tokens + 1) * frame_tokens
+  const int* q_tokens;
+  long frame_tokens;
 };
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -107,7 +111,7 @@ constexpr long attn_piece_floats() { return attn_blocks<HD>() * 64L * (HD / 32 *
 // normalise and write the bf16 output rows (+ LSE); otherwise write the partial
 // (unnormalised O, shift, sum) to `part` for a later merge.  ks / vs are the two
 // LDS buffers of K and V tiles.
-template <int HD>
+template <int HD, bool CAUSAL = false>
 __device__ __forceinline__ void attend_segment(const AttnArgs& a, uint16_t* ks_base, uint16_t* vs_base,
                                                long tile, long t0, long t1, float* part) {
   constexpr int BN = kAttnBN;
@@ -153,9 +157,50 @@ __device__ __forceinline__ void attend_segment(const AttnArgs& a, uint16_t* ks_b
     }
   }
 
+  const long n_kv = a.n_kv;
+  // Frame-causal limits: lim[qb] = keys visible to this lane's query; the workgroup's
+  // smallest and largest limits bound the key range and the tiles that need masking.
+  long lim[QB];
+  long lim_lo = n_kv;
+  if constexpr (CAUSAL) {
+    __shared__ long lim_part[2][NW];
+    long lo = n_kv, hi_ = 1;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const long qrow = qrow0 + 32 * qb;
+      lim[qb] = n_kv;
+      if (qrow < a.n_q) {
+        const long f = static_cast<long>(a.q_tokens[qrow]) / a.frame_tokens;
+        lim[qb] = (f + 1) * a.frame_tokens < n_kv ? (f + 1) * a.frame_tokens : n_kv;
+        lo = lim[qb] < lo ? lim[qb] : lo;
+        hi_ = lim[qb] > hi_ ? lim[qb] : hi_;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const long o_lo = __shfl_xor(lo, off, 64), o_hi = __shfl_xor(hi_, off, 64);
+      lo = o_lo < lo ? o_lo : lo;
+      hi_ = o_hi > hi_ ? o_hi : hi_;
+    }
+    if (lane == 0) {
+      lim_part[0][wave] = lo;
+      lim_part[1][wave] = hi_;
+    }
+    __syncthreads();
+    lo = lim_part[0][0];
+    hi_ = lim_part[1][0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+      lo = lim_part[0][w] < lo ? lim_part[0][w] : lo;
+      hi_ = lim_part[1][w] > hi_ ? lim_part[1][w] : hi_;
+    }
+    lim_lo = lo;
+    const long t_hi = (hi_ + BN - 1) / BN;  // key tiles any query of the workgroup sees
+    t1 = t1 < t_hi ? t1 : t_hi;
+  }
+
   // K/V tiles are fetched with range-checked buffer loads: rows past the end
   // of the cache read as zeros, so prefetches beyond the last tile need no branch.
-  const long n_kv = a.n_kv;
   const int kv_bytes = static_cast<int>(((n_kv - 1) * D + HD) * 2);
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(a.k + head * HD), 0, kv_bytes, kBufferRsrcFlags);
@@ -198,7 +243,15 @@ __device__ __forceinline__ void attend_segment(const AttnArgs& a, uint16_t* ks_b
     }
   };
   auto mask_tail = [&](f32x16* s, long kv0) {
-    if (kv0 + BN > n_kv) {
+    if constexpr (CAUSAL) {
+      if (kv0 + BN > lim_lo) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (kv0 + 8 * (r >> 2) + 4 * hi + (r & 3) >= lim[qb]) s[qb][r] = -__builtin_inff();
+      }
+    } else if (kv0 + BN > n_kv) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -316,7 +369,14 @@ __device__ __forceinline__ void attend_segment(const AttnArgs& a, uint16_t* ks_b
           s_next[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[m], qf[qb][m], m == 0 ? f32x16{} : s_next[qb], 0, 0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (decltype(may_mask)::value) mask_tail(s_next, (t + 1) * BN);
+    // Only the last key tile of the cache can be partial (bidirectional), so only the
+    // iterations whose next tile may be it carry the masking code; frame-causal
+    // limits can fall in any tile.
+    if constexpr (CAUSAL) {
+      if constexpr (decltype(has_next)::value) mask_tail(s_next, (t + 1) * BN);
+    } else if constexpr (decltype(may_mask)::value) {
+      mask_tail(s_next, (t + 1) * BN);
+    }
 
     sstore(vs(b), v_lds, vr);
     sstore(ks(b), k_lds, kr);
@@ -339,8 +399,6 @@ __device__ __forceinline__ void attend_segment(const AttnArgs& a, uint16_t* ks_b
     }
   };
 
-  // Only the last key tile of the cache can be partial, so only the iterations
-  // whose next tile may be it carry the masking code.
   if (t1 - t0 == 1) {
     iteration(t0, Flag<false>{}, Flag<false>{}, Flag<false>{});
   } else {
@@ -402,6 +460,17 @@ __global__ __launch_bounds__(64 * attn_waves<HD>(), attn_min_blocks<HD>()) void 
   const long n_qt = (a.n_q + attn_rows<HD>() - 1) / attn_rows<HD>();
   const long tile = xcd_remap(blockIdx.x, n_qt * a.heads);
   attend_segment<HD>(a, ks, vs, tile, 0, (a.n_kv + kAttnBN - 1) / kAttnBN, nullptr);
+}
+
+// Frame-causal variant: one workgroup per query tile, over the key tiles its
+// queries can see.
+template <int HD>
+__global__ __launch_bounds__(64 * attn_waves<HD>(), attn_min_blocks<HD>()) void attention_causal_kernel(AttnArgs a) {
+  __shared__ __align__(16) uint16_t ks[2 * kAttnBN * (HD + 8)];
+  __shared__ __align__(16) uint16_t vs[2 * kAttnBN * (HD + 32)];
+  const long n_qt = (a.n_q + attn_rows<HD>() - 1) / attn_rows<HD>();
+  const long tile = xcd_remap(blockIdx.x, n_qt * a.heads);
+  attend_segment<HD, true>(a, ks, vs, tile, 0, (a.n_kv + kAttnBN - 1) / kAttnBN, nullptr);
 }
 
 // Split schedule for the last, partly filled round of query tiles.  With C
@@ -576,11 +645,38 @@ size_t attention_workspace_bytes(long n_q, long n_kv, int heads, int head_dim) {
                          : split_bytes<64>(split_plan<64>(n_q, n_kv, heads));
 }
 
+hipError_t launch_attention_causal(const uint16_t* q, const uint16_t* k, const uint16_t* v, long n_q,
+                                   long n_kv, int heads, int head_dim, float scale, const int* q_tokens,
+                                   long frame_tokens, uint16_t* out, const int* out_rows, float* lse,
+                                   hipStream_t s) {
+  AttnArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.n_q = n_q;
+  a.n_kv = n_kv;
+  a.heads = heads;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.out = out;
+  a.out_rows = out_rows;
+  a.lse = lse;
+  a.q_tokens = q_tokens;
+  a.frame_tokens = frame_tokens;
+  if (head_dim == 128) {
+    hipLaunchKernelGGL(attention_causal_kernel<128>, dim3(static_cast<unsigned>(query_tiles<128>(n_q, heads))),
+                       dim3(64 * attn_waves<128>()), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(attention_causal_kernel<64>, dim3(static_cast<unsigned>(query_tiles<64>(n_q, heads))),
+                       dim3(64 * attn_waves<64>()), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, long n_q,
                             long n_kv, int heads, int head_dim, float scale, uint16_t* out,
                             const int* out_rows, float* lse, void* ws, size_t ws_bytes,
                             hipStream_t s) {
-  AttnArgs a;
+  AttnArgs a{};
   a.q = q;
   a.k = k;
   a.v = v;

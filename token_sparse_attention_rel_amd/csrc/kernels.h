@@ -45,14 +45,25 @@ struct QkvOut {
   uint16_t* v;
   int to_cache;     // k/v row r goes to row rows[r]
 };
+// 3D rotary positions applied to Q and K in the epilogue (heads == 0: none).
+struct RopeSpec {
+  int heads = 0;
+  long height = 1;  // token t sits at frame t / (height*width), row (t / width) % height,
+  long width = 1;   // column t % width
+  float log2_base = 0.f;
+};
 hipError_t launch_qkv(const RowSource& src, long n, long dim, const uint16_t* w_qkv,
-                      const QkvOut& out, hipStream_t s);
+                      const QkvOut& out, const RopeSpec& rope, hipStream_t s);
 
 // attention.hip
 // ws == nullptr: one workgroup per query tile.  Otherwise the split schedule of
 // the last round when it pays, with ws of at least attention_workspace_bytes()
 // bytes (hipErrorInvalidValue if smaller).
 size_t attention_workspace_bytes(long n_q, long n_kv, int heads, int head_dim);
+hipError_t launch_attention_causal(const uint16_t* q, const uint16_t* k, const uint16_t* v, long n_q,
+                                   long n_kv, int heads, int head_dim, float scale, const int* q_tokens,
+                                   long frame_tokens, uint16_t* out, const int* out_rows, float* lse,
+                                   hipStream_t s);
 hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, long n_q,
                             long n_kv, int heads, int head_dim, float scale, uint16_t* out,
                             const int* out_rows, float* lse, void* ws, size_t ws_bytes,

@@ -14,6 +14,9 @@
 // pieces of a token row -- straight into the cache row of that token when
 // the cache sync is fused.
 //
+// Optionally the epilogue rotates Q and K by their tokens' 3D positions (rotary
+// embedding over time / height / width channel groups) before rounding.
+//
 // Tile: 128 output features x 128 tokens x 64 (K) per step, 4 waves in a 2x2
 // arrangement, each wave 64 x 64 (2 x 2 MFMA blocks).  Two LDS buffers (one
 // barrier per K step); the registers prefetch the K step after next while the
@@ -47,7 +50,43 @@ struct GemmArgs {
   uint16_t* k;
   uint16_t* v;
   int to_cache;
+  // rotary positions of Q and K (rope_d == 0: none)
+  int rope_d;        // head dim
+  int rope_dt;       // channels of the time axis; the height and width axes get rope_ds each
+  int rope_ds;
+  long rope_hw;      // tokens per frame
+  long rope_w;       // tokens per row
+  float rope_log2_base;
 };
+
+// Rotate the channel pair (a, b) = (feature j, j+1) of a head (j even) by the
+// position of token t along the pair's axis: the time axis owns channels
+// [0, dt), the height axis [dt, dt+ds), the width axis [dt+ds, d); pair i of
+// an axis group of size n turns by pos * base^(-2i/n).
+__device__ __forceinline__ void rope_pair(const GemmArgs& a, long t, int j, float& x0, float& x1) {
+  int i, n;
+  long pos;
+  if (j < a.rope_dt) {
+    i = j >> 1;
+    n = a.rope_dt;
+    pos = t / a.rope_hw;
+  } else if (j < a.rope_dt + a.rope_ds) {
+    i = (j - a.rope_dt) >> 1;
+    n = a.rope_ds;
+    pos = (t / a.rope_w) % (a.rope_hw / a.rope_w);
+  } else {
+    i = (j - a.rope_dt - a.rope_ds) >> 1;
+    n = a.rope_ds;
+    pos = t % a.rope_w;
+  }
+  const float freq = exp2f(-(2.0f * static_cast<float>(i) / static_cast<float>(n)) * a.rope_log2_base);
+  float sn, cs;
+  sincosf(static_cast<float>(pos) * freq, &sn, &cs);
+  const float y0 = x0 * cs - x1 * sn;
+  const float y1 = x0 * sn + x1 * cs;
+  x0 = y0;
+  x1 = y1;
+}
 
 // Word 3 of a raw buffer resource on gfx9-class GPUs; offsets past num_records read zero.
 constexpr int kBufferRsrcFlags = 0x00020000;
@@ -215,8 +254,13 @@ __global__ __launch_bounds__(256, 2) void qkv_gemm_kernel(GemmArgs a) {
           base = part == 1 ? a.k : a.v;
           row = a.to_cache ? t : r;
         }
-        const u32x2 val{pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]),
-                        pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3])};
+        float o[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+        if (a.rope_d && part < 2) {
+          const int hj = static_cast<int>(cc % a.rope_d);
+          rope_pair(a, t, hj, o[0], o[1]);
+          rope_pair(a, t, hj + 2, o[2], o[3]);
+        }
+        const u32x2 val{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
         *reinterpret_cast<u32x2*>(base + row * a.dim + cc) = val;
       }
     }
@@ -224,7 +268,7 @@ __global__ __launch_bounds__(256, 2) void qkv_gemm_kernel(GemmArgs a) {
 }
 
 hipError_t launch_qkv(const RowSource& src, long n, long dim, const uint16_t* w_qkv,
-                      const QkvOut& out, hipStream_t s) {
+                      const QkvOut& out, const RopeSpec& rope, hipStream_t s) {
   GemmArgs a;
   a.x = src.x;
   a.n_x_rows = src.n_x_rows;
@@ -241,6 +285,15 @@ hipError_t launch_qkv(const RowSource& src, long n, long dim, const uint16_t* w_
   a.k = out.k;
   a.v = out.v;
   a.to_cache = out.to_cache;
+  a.rope_d = 0;
+  if (rope.heads > 0) {
+    a.rope_d = static_cast<int>(dim / rope.heads);
+    a.rope_ds = 2 * (a.rope_d / 6);
+    a.rope_dt = a.rope_d - 2 * a.rope_ds;
+    a.rope_hw = rope.height * rope.width;
+    a.rope_w = rope.width;
+    a.rope_log2_base = rope.log2_base;
+  }
   const dim3 grid(static_cast<unsigned>((a.ncols + kGemmBM - 1) / kGemmBM *
                                         ((n + kGemmBN - 1) / kGemmBN)));
   if (src.eps) {

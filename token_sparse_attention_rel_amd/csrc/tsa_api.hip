@@ -158,7 +158,42 @@ tsa_status tsa_qkv_active(const void* x, int x_dtype, int64_t n_x_rows, const in
   if (n == 0) return TSA_OK;
   RowSource src{x, x_dtype, n_x_rows, rows, eps, src_row_offset, sigma};
   tsa::QkvOut out{q_out, k_out, v_out, out_is_cache ? 1 : 0};
-  return from_hip(tsa::launch_qkv(src, n, dim, w_qkv, out, as_stream(stream)));
+  return from_hip(tsa::launch_qkv(src, n, dim, w_qkv, out, tsa::RopeSpec{}, as_stream(stream)));
+}
+
+tsa_status tsa_qkv_active_rope(const void* x, int x_dtype, int64_t n_x_rows, const int32_t* rows,
+                               int64_t n, int64_t dim, const tsa_bf16* w_qkv, tsa_bf16* q_out,
+                               tsa_bf16* k_out, tsa_bf16* v_out, int out_is_cache, int64_t n_cache,
+                               const tsa_bf16* eps, int64_t src_row_offset, float sigma, int heads,
+                               int64_t height, int64_t width, float rope_base, void* stream) {
+  if (heads < 1 || heads > 4096 || dim % heads != 0 || (dim / heads) % 2 != 0 || dim / heads < 6)
+    return TSA_ERR_SHAPE;
+  if (height < 1 || width < 1 || height > kMaxRows || width > kMaxRows || height * width > kMaxRows)
+    return TSA_ERR_SHAPE;
+  if (!(rope_base > 0.f) || isinf(rope_base)) return TSA_ERR_INVALID_ARG;
+  // same validation as tsa_qkv_active
+  if (!x || !w_qkv || !k_out || !v_out) return TSA_ERR_INVALID_ARG;
+  if (x_dtype != TSA_F32 && x_dtype != TSA_BF16) return TSA_ERR_DTYPE;
+  if (eps && x_dtype != TSA_BF16) return TSA_ERR_DTYPE;
+  if (out_is_cache && !rows) return TSA_ERR_INVALID_ARG;
+  if (eps && isnan(sigma)) return TSA_ERR_INVALID_ARG;
+  if (n < 0 || n > kMaxRows || n_x_rows < 0 || n_x_rows > kMaxRows) return TSA_ERR_SHAPE;
+  if (dim <= 0 || dim % 64 != 0 || dim > (int64_t{1} << 20)) return TSA_ERR_SHAPE;
+  if (!rows && n > n_x_rows) return TSA_ERR_SHAPE;
+  if (out_is_cache && (n_cache < 0 || n_cache > kMaxRows)) return TSA_ERR_SHAPE;
+  if (n_x_rows * dim * 2 > kMaxBufferBytes || 3 * dim * dim * 2 > kMaxBufferBytes) return TSA_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(w_qkv) || (q_out && !aligned16(q_out)) || !aligned16(k_out) ||
+      !aligned16(v_out) || (eps && !aligned16(eps)) || (rows && !aligned4(rows)))
+    return TSA_ERR_ALIGNMENT;
+  if (n == 0) return TSA_OK;
+  RowSource src{x, x_dtype, n_x_rows, rows, eps, src_row_offset, sigma};
+  tsa::QkvOut out{q_out, k_out, v_out, out_is_cache ? 1 : 0};
+  tsa::RopeSpec rope;
+  rope.heads = heads;
+  rope.height = height;
+  rope.width = width;
+  rope.log2_base = log2f(rope_base);
+  return from_hip(tsa::launch_qkv(src, n, dim, w_qkv, out, rope, as_stream(stream)));
 }
 
 tsa_status tsa_kv_cache_sync(const tsa_bf16* k_a, const tsa_bf16* v_a, const int32_t* rows,
@@ -198,6 +233,27 @@ tsa_status tsa_sparse_query_attention(const tsa_bf16* q, const tsa_bf16* k_cache
   return from_hip(tsa::launch_attention(q, k_cache, v_cache, n_q, n_kv, heads, head_dim, sc, out,
                                         out_rows, lse_out, workspace, workspace_bytes,
                                         as_stream(stream)));
+}
+
+tsa_status tsa_frame_causal_attention(const tsa_bf16* q, const tsa_bf16* k_cache, const tsa_bf16* v_cache,
+                                      int64_t n_q, int64_t n_kv, int heads, int head_dim, float scale,
+                                      const int32_t* q_tokens, int64_t frame_tokens, tsa_bf16* out,
+                                      const int32_t* out_rows, int64_t n_out, float* lse_out, void* stream) {
+  if (!q || !k_cache || !v_cache || !out || !q_tokens) return TSA_ERR_INVALID_ARG;
+  if (isnan(scale) || isinf(scale)) return TSA_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128) return TSA_ERR_SHAPE;
+  if (heads < 1 || heads > 4096) return TSA_ERR_SHAPE;
+  if (n_q < 0 || n_q > kMaxRows || n_kv < 1 || n_kv > kMaxRows) return TSA_ERR_SHAPE;
+  if (frame_tokens < 1 || frame_tokens > kMaxRows) return TSA_ERR_SHAPE;
+  if (out_rows && (n_out < 0 || n_out > kMaxRows)) return TSA_ERR_SHAPE;
+  if (n_kv * heads * static_cast<int64_t>(head_dim) * 2 > kMaxBufferBytes) return TSA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) || !aligned4(q_tokens) ||
+      (out_rows && !aligned4(out_rows)) || (lse_out && !aligned4(lse_out)))
+    return TSA_ERR_ALIGNMENT;
+  if (n_q == 0) return TSA_OK;
+  const float sc = scale > 0.f ? scale : 1.0f / sqrtf(static_cast<float>(head_dim));
+  return from_hip(tsa::launch_attention_causal(q, k_cache, v_cache, n_q, n_kv, heads, head_dim, sc, q_tokens,
+                                               frame_tokens, out, out_rows, lse_out, as_stream(stream)));
 }
 
 size_t tsa_attention_workspace_bytes(int64_t n_q, int64_t n_kv, int heads, int head_dim) {

@@ -18,9 +18,14 @@ from . import _binding as B
 
 class PrunedAttentionLayer:
     def __init__(self, n: int, dim: int, heads: int, w_qkv: torch.Tensor, device="cuda", *,
-                 split_attention: bool = True):
+                 split_attention: bool = True, rope=None, causal_frame_tokens=None):
+        """``rope = (height, width, base)`` rotates Q and K by their tokens' 3D positions
+        (the cache then holds rotated K); ``causal_frame_tokens`` makes the attention
+        frame-causal (a query sees the frames up to its own)."""
         if dim % heads:
             raise ValueError("dim must be a multiple of heads")
+        self.rope = rope
+        self.causal_frame_tokens = causal_frame_tokens
         self.n, self.dim, self.heads = n, dim, heads
         self.head_dim = dim // heads
         self.device = torch.device(device)
@@ -62,10 +67,31 @@ class PrunedAttentionLayer:
 
     # ---------------------------------------------------------------- state
 
+    def _qkv(self, x, rows, n, **kw):
+        if self.rope is None:
+            B.qkv_active(x, rows, n, self.w_qkv, **kw)
+        else:
+            h, w, base = self.rope
+            B.qkv_active_rope(x, rows, n, self.w_qkv, self.heads, h, w, rope_base=base, **kw)
+
+    def _attend(self, n_q, out, q_tokens, rows=None, stream=None):
+        """Attention of the n_q queries in q_a (tokens q_tokens) over the cache."""
+        if self.causal_frame_tokens is None:
+            B.sparse_query_attention(self.q_a, self.k_cache, self.v_cache, n_q, self.heads, self.head_dim,
+                                     out, out_rows=rows, workspace=self.attention_workspace(n_q),
+                                     stream=stream)
+        else:
+            B.frame_causal_attention(self.q_a, self.k_cache, self.v_cache, n_q, self.heads, self.head_dim,
+                                     q_tokens, self.causal_frame_tokens, out, out_rows=rows, stream=stream)
+
+    def _identity_rows(self):
+        if getattr(self, "_iota", None) is None:
+            self._iota = torch.arange(self.n, dtype=torch.int32, device=self.device)
+        return self._iota
+
     def init_cache(self, x_prev: torch.Tensor, stream=None) -> None:
         """K/V cache = projections of every token of x_prev (the start of a run)."""
-        B.qkv_active(x_prev, None, self.n, self.w_qkv, q_out=None, k_out=self.k_cache,
-                     v_out=self.v_cache, stream=stream)
+        self._qkv(x_prev, None, self.n, q_out=None, k_out=self.k_cache, v_out=self.v_cache, stream=stream)
 
     def _compact_bufs(self):
         if self._k_a is None:
@@ -100,19 +126,14 @@ class PrunedAttentionLayer:
             return
         idx = self.idx
         if fused:
-            B.qkv_active(x_cur, idx, n_active, self.w_qkv, q_out=self.q_a, k_out=self.k_cache,
-                         v_out=self.v_cache, out_is_cache=True, n_cache=self.n, stream=stream)
-            B.sparse_query_attention(self.q_a, self.k_cache, self.v_cache, n_active, self.heads,
-                                     self.head_dim, self.out, out_rows=idx,
-                                     workspace=self.attention_workspace(n_active), stream=stream)
+            self._qkv(x_cur, idx, n_active, q_out=self.q_a, k_out=self.k_cache, v_out=self.v_cache,
+                      out_is_cache=True, n_cache=self.n, stream=stream)
+            self._attend(n_active, self.out, idx, rows=idx, stream=stream)
         else:
             k_a, v_a, o_a = self._compact_bufs()
-            B.qkv_active(x_cur, idx, n_active, self.w_qkv, q_out=self.q_a, k_out=k_a, v_out=v_a,
-                         stream=stream)
+            self._qkv(x_cur, idx, n_active, q_out=self.q_a, k_out=k_a, v_out=v_a, stream=stream)
             B.kv_cache_sync(k_a, v_a, idx, n_active, self.k_cache, self.v_cache, stream=stream)
-            B.sparse_query_attention(self.q_a, self.k_cache, self.v_cache, n_active, self.heads,
-                                     self.head_dim, o_a, workspace=self.attention_workspace(n_active),
-                                     stream=stream)
+            self._attend(n_active, o_a, idx, stream=stream)
             B.scatter_out(o_a, idx, n_active, self.out, stream=stream)
 
     def step_topk(self, x_cur, x_ref, k: int, *, fused=True, stream=None) -> None:
@@ -153,28 +174,23 @@ class PrunedAttentionLayer:
         return k
 
     def _lipar_forward(self, x, eps, hw, k, sigma, stream):
-        B.qkv_active(x, self.idx, k, self.w_qkv, q_out=self.q_a, k_out=self.k_cache,
-                     v_out=self.v_cache, out_is_cache=True, n_cache=self.n, stream=stream)
+        self._qkv(x, self.idx, k, q_out=self.q_a, k_out=self.k_cache, v_out=self.v_cache,
+                  out_is_cache=True, n_cache=self.n, stream=stream)
         n_p = self.n - k
         if n_p:
-            B.qkv_active(x, self.pidx, n_p, self.w_qkv, q_out=None, k_out=self.k_cache,
-                         v_out=self.v_cache, out_is_cache=True, n_cache=self.n, eps=eps,
-                         src_row_offset=hw, sigma=sigma, stream=stream)
+            self._qkv(x, self.pidx, n_p, q_out=None, k_out=self.k_cache, v_out=self.v_cache,
+                      out_is_cache=True, n_cache=self.n, eps=eps, src_row_offset=hw, sigma=sigma,
+                      stream=stream)
         if k:
-            B.sparse_query_attention(self.q_a, self.k_cache, self.v_cache, k, self.heads,
-                                     self.head_dim, self.out, out_rows=self.idx,
-                                     workspace=self.attention_workspace(k), stream=stream)
+            self._attend(k, self.out, self.idx, rows=self.idx, stream=stream)
 
     # ------------------------------------------------------- sampling loop
 
     def dense_forward(self, x, stream=None) -> None:
         """Every token active: QKV of all rows straight into the cache, attention of all
         queries written in token order (no selection, no index indirection)."""
-        B.qkv_active(x, None, self.n, self.w_qkv, q_out=self.q_a, k_out=self.k_cache,
-                     v_out=self.v_cache, stream=stream)
-        B.sparse_query_attention(self.q_a, self.k_cache, self.v_cache, self.n, self.heads,
-                                 self.head_dim, self.out, workspace=self.attention_workspace(self.n),
-                                 stream=stream)
+        self._qkv(x, None, self.n, q_out=self.q_a, k_out=self.k_cache, v_out=self.v_cache, stream=stream)
+        self._attend(self.n, self.out, self._identity_rows(), stream=stream)
 
     def hsa_run(self, x, periods, sigmas, window: int, group_counts, group_periods, *,
                 stream=None, on_step=None) -> None:
