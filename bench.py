@@ -235,7 +235,9 @@ def bench_step(args, torch, tsa, cfg):
     dev = torch.device("cuda:0")
     inp = generate.step_inputs(cfg, args.seed)
     layer = tsa.PrunedAttentionLayer(cfg.n, cfg.dim, cfg.heads, inp["w_qkv"].to(dev), device=dev,
-                                     split_attention=args.attn_schedule == "split")
+                                     split_attention=args.attn_schedule == "split",
+                                     rope=(cfg.height, cfg.width, 10000.0) if cfg.rope else None,
+                                     causal_frame_tokens=cfg.hw if cfg.causal else None)
     xp = inp["x_prev"].to(dev)
     xc = inp["x_cur"].to(dev)
     layer.init_cache(xp)
@@ -256,12 +258,16 @@ def bench_step(args, torch, tsa, cfg):
         layer.select(xc, xp, k=k)
         t_sel.stop()
         t_qkv.start()
-        tsa.qkv_active(xc, layer.idx, k, layer.w_qkv, q_out=layer.q_a, k_out=layer.k_cache,
-                       v_out=layer.v_cache, out_is_cache=True, n_cache=cfg.n)
+        layer._qkv(xc, layer.idx, k, q_out=layer.q_a, k_out=layer.k_cache, v_out=layer.v_cache,
+                   out_is_cache=True, n_cache=cfg.n)
         t_qkv.stop()
         t_att.start()
-        tsa.sparse_query_attention(layer.q_a, layer.k_cache, layer.v_cache, k, cfg.heads,
-                                   cfg.head_dim, layer.out, out_rows=layer.idx, workspace=attn_ws)
+        if cfg.causal:
+            tsa.frame_causal_attention(layer.q_a, layer.k_cache, layer.v_cache, k, cfg.heads, cfg.head_dim,
+                                       layer.idx, cfg.hw, layer.out, out_rows=layer.idx)
+        else:
+            tsa.sparse_query_attention(layer.q_a, layer.k_cache, layer.v_cache, k, cfg.heads,
+                                       cfg.head_dim, layer.out, out_rows=layer.idx, workspace=attn_ws)
         t_att.stop()
         t_step.stop()
     torch.cuda.synchronize()
@@ -271,6 +277,13 @@ def bench_step(args, torch, tsa, cfg):
     t_att_mean = s_att["mean"]
 
     flops = cfg.attn_flops(k)
+    if cfg.causal:
+        # algorithmic work of the frame-causal attention: each query's visible keys only
+        import numpy as np
+
+        fr = layer.idx[:k].cpu().numpy().astype(np.int64) // cfg.hw
+        visible = np.minimum((fr + 1) * cfg.hw, cfg.n)
+        flops = int(4 * visible.sum() * cfg.head_dim * cfg.heads)
     dense = None
     if not args.no_dense:
         # dense layer: the same QKV and attention kernels over every token, no selection
@@ -303,13 +316,17 @@ def bench_step(args, torch, tsa, cfg):
         "config": {
             "workload": f"{cfg.name}: F={cfg.frames} H={cfg.height} W={cfg.width} -> N={cfg.n} tokens, "
                         f"D={cfg.dim}, {cfg.heads} heads x d={cfg.head_dim}, {cfg.active_pct}% active "
-                        f"(k={k}), {cfg.static_pct}% static tokens, full bidirectional attention",
+                        f"(k={k}), {cfg.static_pct}% static tokens, "
+                        + ("3D rotary positions on Q/K, frame-causal attention" if cfg.rope or cfg.causal
+                           else "full bidirectional attention"),
             "n_tokens": cfg.n,
             "n_active": k,
             "dim": cfg.dim,
             "heads": cfg.heads,
             "head_dim": cfg.head_dim,
             "seed": args.seed,
+            "rope": cfg.rope,
+            "frame_causal": cfg.causal,
         },
         "attention_schedule": ("one workgroup per query tile, last round split into key ranges"
                                if attn_ws is not None else "one workgroup per query tile"),
@@ -336,7 +353,11 @@ def bench_step(args, torch, tsa, cfg):
             "launch_ms_mean_events": round(t_att_mean, 5),
         },
     }
-    if not args.no_cpu_baseline:
+    if cfg.causal:
+        rec["roofline"]["kernel"] = ("attention_causal_kernel<128> (active queries x the keys of their "
+                                     "frames and earlier, fused scatter)")
+        rec["attention_schedule"] = "one workgroup per query tile, key loop bounded by its queries' frames"
+    if not args.no_cpu_baseline and not (cfg.rope or cfg.causal):
         rec["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_rows)
     return rec
 

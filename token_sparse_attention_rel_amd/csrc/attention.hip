@@ -463,13 +463,18 @@ __global__ __launch_bounds__(64 * attn_waves<HD>(), attn_min_blocks<HD>()) void 
 }
 
 // Frame-causal variant: one workgroup per query tile, over the key tiles its
-// queries can see.
+// queries can see.  Queries usually come in token order, so later query tiles
+// see more keys.  Blocks take the tiles latest-first, all heads of one query
+// tile before the next: the long tiles start first on every XCD and the short
+// ones fill in behind them (a longest-first schedule; with the XCD-contiguous
+// order of the bidirectional kernel one XCD got far more work than another).
 template <int HD>
 __global__ __launch_bounds__(64 * attn_waves<HD>(), attn_min_blocks<HD>()) void attention_causal_kernel(AttnArgs a) {
   __shared__ __align__(16) uint16_t ks[2 * kAttnBN * (HD + 8)];
   __shared__ __align__(16) uint16_t vs[2 * kAttnBN * (HD + 32)];
   const long n_qt = (a.n_q + attn_rows<HD>() - 1) / attn_rows<HD>();
-  const long tile = xcd_remap(blockIdx.x, n_qt * a.heads);
+  const long b = blockIdx.x;
+  const long tile = (b % a.heads) * n_qt + (n_qt - 1 - b / a.heads);
   attend_segment<HD, true>(a, ks, vs, tile, 0, (a.n_kv + kAttnBN - 1) / kAttnBN, nullptr);
 }
 

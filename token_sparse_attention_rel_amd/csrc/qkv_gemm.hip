@@ -59,29 +59,28 @@ struct GemmArgs {
   float rope_log2_base;
 };
 
-// Rotate the channel pair (a, b) = (feature j, j+1) of a head (j even) by the
-// position of token t along the pair's axis: the time axis owns channels
+// Rotate the channel pair (x0, x1) = (feature j, j+1) of a head (j even) by the
+// position of its token along the pair's axis: the time axis owns channels
 // [0, dt), the height axis [dt, dt+ds), the width axis [dt+ds, d); pair i of
-// an axis group of size n turns by pos * base^(-2i/n).
-__device__ __forceinline__ void rope_pair(const GemmArgs& a, long t, int j, float& x0, float& x1) {
-  int i, n;
-  long pos;
+// an axis group of size n turns by pos * base^(-2i/n).  pos = (frame, row, column).
+__device__ __forceinline__ void rope_pair(const GemmArgs& a, const float pos[3], int j, float& x0, float& x1) {
+  int i, n, ax;
   if (j < a.rope_dt) {
     i = j >> 1;
     n = a.rope_dt;
-    pos = t / a.rope_hw;
+    ax = 0;
   } else if (j < a.rope_dt + a.rope_ds) {
     i = (j - a.rope_dt) >> 1;
     n = a.rope_ds;
-    pos = (t / a.rope_w) % (a.rope_hw / a.rope_w);
+    ax = 1;
   } else {
     i = (j - a.rope_dt - a.rope_ds) >> 1;
     n = a.rope_ds;
-    pos = t % a.rope_w;
+    ax = 2;
   }
   const float freq = exp2f(-(2.0f * static_cast<float>(i) / static_cast<float>(n)) * a.rope_log2_base);
   float sn, cs;
-  sincosf(static_cast<float>(pos) * freq, &sn, &cs);
+  sincosf(pos[ax] * freq, &sn, &cs);
   const float y0 = x0 * cs - x1 * sn;
   const float y1 = x0 * sn + x1 * cs;
   x0 = y0;
@@ -237,6 +236,15 @@ __global__ __launch_bounds__(256, 2) void qkv_gemm_kernel(GemmArgs a) {
     const long r = t_base + wt * 64 + j * 32 + l32;
     if (r >= a.n) continue;
     const long t = a.rows ? static_cast<long>(a.rows[r]) : r;
+    float pos[3] = {0.f, 0.f, 0.f};
+    if (a.rope_d) {
+      const unsigned tu = static_cast<unsigned>(t), hw = static_cast<unsigned>(a.rope_hw),
+                     w = static_cast<unsigned>(a.rope_w);
+      const unsigned in_frame = tu % hw;
+      pos[0] = static_cast<float>(tu / hw);
+      pos[1] = static_cast<float>(in_frame / w);
+      pos[2] = static_cast<float>(in_frame % w);
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
 #pragma unroll
@@ -257,8 +265,8 @@ __global__ __launch_bounds__(256, 2) void qkv_gemm_kernel(GemmArgs a) {
         float o[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
         if (a.rope_d && part < 2) {
           const int hj = static_cast<int>(cc % a.rope_d);
-          rope_pair(a, t, hj, o[0], o[1]);
-          rope_pair(a, t, hj + 2, o[2], o[3]);
+          rope_pair(a, pos, hj, o[0], o[1]);
+          rope_pair(a, pos, hj + 2, o[2], o[3]);
         }
         const u32x2 val{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
         *reinterpret_cast<u32x2*>(base + row * a.dim + cc) = val;

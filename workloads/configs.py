@@ -36,6 +36,8 @@ class Config:
     window: int = 0  # "hsa_loop": the first and last `window` steps run dense
     tau_short: float = 0.0  # "lipar_lif": threshold on the L1 change against the previous frame
     tau_long: float = 0.0  # "lipar_lif": threshold on the L1 change against the last kept frame
+    rope: bool = False  # "step": 3D rotary positions on Q and K (base 10000)
+    causal: bool = False  # "step": frame-causal attention (a query sees the frames up to its own)
 
     @property
     def n(self) -> int:
@@ -81,6 +83,9 @@ CONFIGS = {
     "tiny": Config("tiny", "step", 4, 8, 8, 128, 2, 64, "fp32", static_pct=70, active_pct=25),
     # Wan-1.3B-like grid 21x30x52, 30% active (the headline workload).
     "wan13b": Config("wan13b", "step", 21, 30, 52, 1536, 12, 128, "bf16", static_pct=70, active_pct=30),
+    # The headline grid with 3D rotary positions and frame-causal attention.
+    "wan13b_rc": Config("wan13b_rc", "step", 21, 30, 52, 1536, 12, 128, "bf16", static_pct=70, active_pct=30,
+                        rope=True, causal=True),
     # 21x45x80 grid at model dim 5120, 20% active.
     "large": Config("large", "step", 21, 45, 80, 5120, 40, 128, "bf16", static_pct=80, active_pct=20),
     # HSA schedule loop on the Wan-1.3B-like grid: T=8, groups 25/25/50 % with budgets 8/4/2.
