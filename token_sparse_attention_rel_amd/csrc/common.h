@@ -40,6 +40,22 @@ __device__ __forceinline__ void unpack8(const u32x4 v, float* f) {
   }
 }
 
+// LIPAR recovery of 8 bf16 elements: bf16((1 - s) * clean + s * noise), the
+// products and sum in fp32 (one fused multiply-add), rounded to nearest even.
+__device__ __forceinline__ u32x4 recover8(const u32x4 clean, const u32x4 noise, float one_m_s, float s) {
+  float c[8], e[8];
+  unpack8(clean, c);
+  unpack8(noise, e);
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = fmaf(one_m_s, c[2 * i], s * e[2 * i]);
+    const float b = fmaf(one_m_s, c[2 * i + 1], s * e[2 * i + 1]);
+    r[i] = pack_bf16x2(a, b);
+  }
+  return r;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);

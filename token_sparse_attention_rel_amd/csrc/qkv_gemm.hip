@@ -17,19 +17,30 @@
 // Optionally the epilogue rotates Q and K by their tokens' 3D positions (rotary
 // embedding over time / height / width channel groups) before rounding.
 //
-// Tile: 128 output features x 128 tokens x 64 (K) per step, 4 waves in a 2x2
-// arrangement, each wave 64 x 64 (2 x 2 MFMA blocks).  Two LDS buffers (one
+// Tile: 256 output features x 256 tokens x 64 (K) per step, 8 waves in a 4x2
+// arrangement, each wave 64 features x 128 tokens (2 x 4 MFMA blocks): six
+// 16-byte LDS reads feed eight MFMAs, and each staged K slice is shared by 256
+// columns and 256 tokens.  Two LDS buffers (144 KB, one workgroup per CU, one
 // barrier per K step); the registers prefetch the K step after next while the
-// current one is multiplied.  bf16 rows arrive through range-checked buffer
-// loads (invalid rows read as zeros, no per-step selects).
+// current one is multiplied.  bf16 rows (and the recovery noise) arrive through
+// range-checked buffer loads (invalid rows read as zeros, no per-step selects).
 #include "common.h"
 #include "kernels.h"
 
 namespace tsa {
 
-constexpr int kGemmBM = 128;  // output features per block
-constexpr int kGemmBN = 128;  // tokens per block
+constexpr int kGemmBM = 256;  // output features per block
+constexpr int kGemmBN = 256;  // tokens per block
 constexpr int kGemmBK = 64;
+constexpr int kGemmThreads = 512;
+constexpr int kGemmWavesT = 2;                       // waves along tokens (4 along features)
+constexpr int kWaveBF = 2;                           // 32-feature MFMA blocks per wave
+constexpr int kWaveBT = 4;                           // 32-token MFMA blocks per wave
+constexpr int kLoadRows = kGemmThreads / 8;          // tile rows staged per load round
+constexpr int kLoadW = kGemmBM / kLoadRows;          // 16-byte W chunks per thread and K step
+constexpr int kLoadA = kGemmBN / kLoadRows;          // 16-byte A chunks per thread and K step
+static_assert((kGemmThreads / 64) / kGemmWavesT * kWaveBF * 32 == kGemmBM, "feature tiling");
+static_assert(kGemmWavesT * kWaveBT * 32 == kGemmBN, "token tiling");
 constexpr int kGemmLD = kGemmBK + 8;  // LDS row stride (elements): 144 B, conflict-free 16-byte reads
 
 enum { kSrcBf16 = 0, kSrcF32 = 1, kSrcRecover = 2 };
@@ -94,37 +105,10 @@ constexpr int kOutOfRange = 0x7FFFFFF0;
 
 // Token tiles handled together per XCD: the workgroups that run at the same
 // time on one XCD then share few W panels and few token tiles in its L2.
-constexpr int kTokGroup = 8;
+constexpr int kTokGroup = 4;
 
 template <int SRC>
-__device__ __forceinline__ u32x4 load_a_chunk_slow(const GemmArgs& a, long tok, bool valid,
-                                                   bool has_clean, long k0) {
-  if (!valid) return u32x4{0u, 0u, 0u, 0u};
-  if (SRC == kSrcF32) {
-    const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(a.x) + tok * a.dim + k0);
-    const f32x4 lo = p[0], hi = p[1];
-    return u32x4{pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]), pack_bf16x2(hi[0], hi[1]),
-                 pack_bf16x2(hi[2], hi[3])};
-  } else {
-    const u32x4 e = *reinterpret_cast<const u32x4*>(a.eps + tok * a.dim + k0);
-    const u32x4 c = has_clean ? *reinterpret_cast<const u32x4*>(
-                                    static_cast<const uint16_t*>(a.x) + (tok - a.src_off) * a.dim + k0)
-                              : u32x4{0u, 0u, 0u, 0u};
-    float fc[8], fe[8];
-    unpack8(c, fc);
-    unpack8(e, fe);
-    const float oms = 1.0f - a.sigma;
-    u32x4 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      r[i] = pack_bf16x2(fmaf(oms, fc[2 * i], a.sigma * fe[2 * i]),
-                         fmaf(oms, fc[2 * i + 1], a.sigma * fe[2 * i + 1]));
-    return r;
-  }
-}
-
-template <int SRC>
-__global__ __launch_bounds__(256, 2) void qkv_gemm_kernel(GemmArgs a) {
+__global__ __launch_bounds__(kGemmThreads, 1) void qkv_gemm_kernel(GemmArgs a) {
   __shared__ __align__(16) uint16_t ws[2][kGemmBM * kGemmLD];
   __shared__ __align__(16) uint16_t as[2][kGemmBN * kGemmLD];
 
@@ -145,7 +129,7 @@ __global__ __launch_bounds__(256, 2) void qkv_gemm_kernel(GemmArgs a) {
   const long t_base = tok_tile * kGemmBN;            // compact token row
   const long c_end = a.col0 + a.ncols;
 
-  // Loader slots: rows lrow + 32*j of each tile, 16-byte chunk (tid & 7) of the K slice.
+  // Loader slots: rows lrow + kLoadRows*j of each tile, 16-byte chunk (tid & 7) of the K slice.
   const int lrow = tid >> 3;
   const int lcol = (tid & 7) * 8;
   const long dim = a.dim;
@@ -153,48 +137,87 @@ __global__ __launch_bounds__(256, 2) void qkv_gemm_kernel(GemmArgs a) {
       const_cast<uint16_t*>(a.w), 0, static_cast<int>(3 * dim * dim * 2), kBufferRsrcFlags);
   const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<void*>(a.x), 0, static_cast<int>(a.n_x_rows * dim * 2), kBufferRsrcFlags);
-  int w_off[4], x_off[4];
-  long tok[4];
-  bool tvalid[4], tclean[4];
+  // The A chunks are loaded raw and converted only when written to LDS, one K
+  // step later, so the conversion never waits on a load just issued.
+  //   bf16:     raw[0] = the row chunk
+  //   recovery: raw[0] = clean chunk (zeros when the token has no clean row), raw[1] = noise
+  //   fp32:     raw[0], raw[1] = the two 16-byte halves (invalid rows read row 0, zeroed at the store)
+  const __amdgpu_buffer_rsrc_t ers = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.eps), 0, SRC == kSrcRecover ? static_cast<int>(a.n_x_rows * dim * 2) : 0,
+      kBufferRsrcFlags);
+  int w_off[kLoadW], x_off[kLoadA], e_off[kLoadA];
+  long ftok[kLoadA];
+  bool tvalid[kLoadA];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const long c = c_base + lrow + 32 * j;
+  for (int j = 0; j < kLoadW; ++j) {
+    const long c = c_base + lrow + kLoadRows * j;
     w_off[j] = c < c_end ? static_cast<int>((c * dim + lcol) * 2) : kOutOfRange;
-    const long r = t_base + lrow + 32 * j;
+  }
+#pragma unroll
+  for (int j = 0; j < kLoadA; ++j) {
+    const long r = t_base + lrow + kLoadRows * j;
     tvalid[j] = r < a.n;
-    tok[j] = tvalid[j] ? (a.rows ? static_cast<long>(a.rows[r]) : r) : 0;
-    x_off[j] = tvalid[j] ? static_cast<int>((tok[j] * dim + lcol) * 2) : kOutOfRange;
-    const long src = tok[j] - a.src_off;
-    tclean[j] = src >= 0 && src < a.n_x_rows;
+    const long tok = tvalid[j] ? (a.rows ? static_cast<long>(a.rows[r]) : r) : 0;
+    ftok[j] = tok;
+    if constexpr (SRC == kSrcRecover) {
+      const long src = tok - a.src_off;
+      const bool clean = tvalid[j] && src >= 0 && src < a.n_x_rows;
+      x_off[j] = clean ? static_cast<int>((src * dim + lcol) * 2) : kOutOfRange;
+      e_off[j] = tvalid[j] ? static_cast<int>((tok * dim + lcol) * 2) : kOutOfRange;
+    } else {
+      x_off[j] = tvalid[j] ? static_cast<int>((tok * dim + lcol) * 2) : kOutOfRange;
+      e_off[j] = kOutOfRange;
+    }
   }
 
-  u32x4 wreg[4], areg[4];
+  constexpr int kRaw = SRC == kSrcBf16 ? 1 : 2;
+  u32x4 wreg[kLoadW], araw[kLoadA][kRaw];
   auto load_tiles = [&](long k0) {
     const int so = static_cast<int>(k0 * 2);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kLoadW; ++j)
       wreg[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, w_off[j], so, 0));
-      if constexpr (SRC == kSrcBf16)
-        areg[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, x_off[j], so, 0));
-      else
-        areg[j] = load_a_chunk_slow<SRC>(a, tok[j], tvalid[j], tclean[j], k0 + lcol);
+#pragma unroll
+    for (int j = 0; j < kLoadA; ++j) {
+      if constexpr (SRC == kSrcF32) {
+        const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(a.x) + ftok[j] * dim + k0 + lcol);
+        araw[j][0] = __builtin_bit_cast(u32x4, p[0]);
+        araw[j][1] = __builtin_bit_cast(u32x4, p[1]);
+      } else {
+        araw[j][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, x_off[j], so, 0));
+        if constexpr (SRC == kSrcRecover)
+          araw[j][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ers, e_off[j], so, 0));
+      }
+    }
+  };
+  auto a_chunk = [&](int j) -> u32x4 {
+    if constexpr (SRC == kSrcBf16) {
+      return araw[j][0];
+    } else if constexpr (SRC == kSrcRecover) {
+      return recover8(araw[j][0], araw[j][1], 1.0f - a.sigma, a.sigma);
+    } else {
+      const f32x4 lo = __builtin_bit_cast(f32x4, araw[j][0]), hi = __builtin_bit_cast(f32x4, araw[j][1]);
+      const u32x4 v{pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]), pack_bf16x2(hi[0], hi[1]),
+                    pack_bf16x2(hi[2], hi[3])};
+      return tvalid[j] ? v : u32x4{0u, 0u, 0u, 0u};
     }
   };
   auto store_tiles = [&](int buf) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      *reinterpret_cast<u32x4*>(&ws[buf][(lrow + 32 * j) * kGemmLD + lcol]) = wreg[j];
-      *reinterpret_cast<u32x4*>(&as[buf][(lrow + 32 * j) * kGemmLD + lcol]) = areg[j];
-    }
+    for (int j = 0; j < kLoadW; ++j)
+      *reinterpret_cast<u32x4*>(&ws[buf][(lrow + kLoadRows * j) * kGemmLD + lcol]) = wreg[j];
+#pragma unroll
+    for (int j = 0; j < kLoadA; ++j)
+      *reinterpret_cast<u32x4*>(&as[buf][(lrow + kLoadRows * j) * kGemmLD + lcol]) = a_chunk(j);
   };
 
-  const int wc = wave >> 1;  // feature half of the block
-  const int wt = wave & 1;   // token half of the block
-  f32x16 acc[2][2];
+  const int wc = wave / kGemmWavesT;  // feature quarter of the block
+  const int wt = wave % kGemmWavesT;  // token half of the block
+  f32x16 acc[kWaveBF][kWaveBT];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kWaveBF; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < kWaveBT; ++j) acc[i][j] = f32x16{};
 
   const long n_k = dim / kGemmBK;
   load_tiles(0);
@@ -209,17 +232,17 @@ __global__ __launch_bounds__(256, 2) void qkv_gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int kk16 = 0; kk16 < kGemmBK / 16; ++kk16) {
       const int kk = kk16 * 16 + khalf;
-      bf16x8 fw[2], ft[2];
+      bf16x8 fw[kWaveBF], ft[kWaveBT];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        fw[i] = *reinterpret_cast<const bf16x8*>(&ws[buf][(wc * 64 + i * 32 + l32) * kGemmLD + kk]);
+      for (int i = 0; i < kWaveBF; ++i)
+        fw[i] = *reinterpret_cast<const bf16x8*>(&ws[buf][((wc * kWaveBF + i) * 32 + l32) * kGemmLD + kk]);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        ft[j] = *reinterpret_cast<const bf16x8*>(&as[buf][(wt * 64 + j * 32 + l32) * kGemmLD + kk]);
+      for (int j = 0; j < kWaveBT; ++j)
+        ft[j] = *reinterpret_cast<const bf16x8*>(&as[buf][((wt * kWaveBT + j) * 32 + l32) * kGemmLD + kk]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < kWaveBF; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < kWaveBT; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[i], ft[j], acc[i][j], 0, 0, 0);
     }
     // Stage K slice ks+1 into the other buffer (last read in step ks-1, before the
@@ -232,8 +255,8 @@ __global__ __launch_bounds__(256, 2) void qkv_gemm_kernel(GemmArgs a) {
   // Epilogue: lane holds token (l32) and features 8g + 4*(lane/32) + 0..3 of each 32-block.
   const int fsub = (lane >> 5) * 4;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const long r = t_base + wt * 64 + j * 32 + l32;
+  for (int j = 0; j < kWaveBT; ++j) {
+    const long r = t_base + (wt * kWaveBT + j) * 32 + l32;
     if (r >= a.n) continue;
     const long t = a.rows ? static_cast<long>(a.rows[r]) : r;
     float pos[3] = {0.f, 0.f, 0.f};
@@ -246,10 +269,10 @@ __global__ __launch_bounds__(256, 2) void qkv_gemm_kernel(GemmArgs a) {
       pos[2] = static_cast<float>(in_frame % w);
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < kWaveBF; ++i) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const long c = c_base + wc * 64 + i * 32 + g * 8 + fsub;
+        const long c = c_base + (wc * kWaveBF + i) * 32 + g * 8 + fsub;
         if (c >= c_end) continue;
         const long part = c / a.dim;
         const long cc = c - part * a.dim;
@@ -305,11 +328,11 @@ hipError_t launch_qkv(const RowSource& src, long n, long dim, const uint16_t* w_
   const dim3 grid(static_cast<unsigned>((a.ncols + kGemmBM - 1) / kGemmBM *
                                         ((n + kGemmBN - 1) / kGemmBN)));
   if (src.eps) {
-    hipLaunchKernelGGL(qkv_gemm_kernel<kSrcRecover>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(qkv_gemm_kernel<kSrcRecover>, grid, dim3(kGemmThreads), 0, s, a);
   } else if (src.x_dtype == kDtypeF32) {
-    hipLaunchKernelGGL(qkv_gemm_kernel<kSrcF32>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(qkv_gemm_kernel<kSrcF32>, grid, dim3(kGemmThreads), 0, s, a);
   } else {
-    hipLaunchKernelGGL(qkv_gemm_kernel<kSrcBf16>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(qkv_gemm_kernel<kSrcBf16>, grid, dim3(kGemmThreads), 0, s, a);
   }
   return hipGetLastError();
 }

@@ -15,21 +15,6 @@ namespace tsa {
 
 constexpr int kRowsPerBlock = 4;
 
-__device__ __forceinline__ u32x4 recover8(const u32x4 clean, const u32x4 noise, float one_m_s,
-                                          float s) {
-  float c[8], e[8];
-  unpack8(clean, c);
-  unpack8(noise, e);
-  u32x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float a = fmaf(one_m_s, c[2 * i], s * e[2 * i]);
-    const float b = fmaf(one_m_s, c[2 * i + 1], s * e[2 * i + 1]);
-    r[i] = pack_bf16x2(a, b);
-  }
-  return r;
-}
-
 template <bool RECOVER, int J>
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __restrict__ x,
                                                           long n_x_rows,
