@@ -93,7 +93,7 @@ def _exact_score_rows(values, dim=64, seed=0):
     return x_cur, x_ref
 
 
-@pytest.mark.parametrize("n", [1, 7, 100, 4096, 4099, 12000, 20000, 32768, 40000])
+@pytest.mark.parametrize("n", [1, 7, 100, 4096, 4099, 12000, 20000, 32760, 32768, 32769, 40000, 100001])
 def test_topk_select_and_compact_bit_exact_with_ties(n):
     t = tsa()
     r = np.random.default_rng(n)
@@ -124,7 +124,32 @@ def test_topk_select_and_compact_bit_exact_with_ties(n):
         assert np.array_equal(pidx.cpu().numpy()[:n - k], wp)
 
 
-@pytest.mark.parametrize("n", [5, 1023, 4096, 30001])
+@pytest.mark.parametrize("n,k", [(32760, 9828), (100001, 30000), (118800, 45619), (65536, 1)])
+def test_topk_distinct_scores_multi_chunk(n, k):
+    """Continuous scores (no ties): the selected set is the top k of the kernel's own fp32
+    scores, decided by the oracle on those same values."""
+    t = tsa()
+    g = torch.Generator().manual_seed(n)
+    x_ref = torch.randn(n, 64, generator=g).to(torch.bfloat16)
+    x_cur = (x_ref.float() + 0.3 * torch.randn(n, 64, generator=g)).to(torch.bfloat16)
+    scores = torch.empty(n, device="cuda")
+    mask = torch.empty(n, dtype=torch.uint8, device="cuda")
+    idx = torch.empty(n, dtype=torch.int32, device="cuda")
+    pidx = torch.empty(n, dtype=torch.int32, device="cuda")
+    na = torch.empty(1, dtype=torch.int32, device="cuda")
+    t.select_active(G.dev(x_cur), G.dev(x_ref), 0, t.SELECT_TOPK, k=k, scores_out=scores, mask_out=mask,
+                    idx_out=idx, pidx_out=pidx, n_active_out=na)
+    torch.cuda.synchronize()
+    s64 = G.host64(scores)
+    want = ref.select_topk(s64, k)
+    wi, wp = ref.compact(want)
+    assert np.array_equal(mask.cpu().numpy().astype(bool), want)
+    assert int(na.item()) == k
+    assert np.array_equal(idx.cpu().numpy()[:k], wi)
+    assert np.array_equal(pidx.cpu().numpy()[:n - k], wp)
+
+
+@pytest.mark.parametrize("n", [5, 1023, 4096, 30001, 70001])
 def test_threshold_mask_schedule_modes_bit_exact(n):
     t = tsa()
     r = np.random.default_rng(7 + n)
