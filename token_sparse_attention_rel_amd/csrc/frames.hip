@@ -11,7 +11,7 @@
 // only when both are below their thresholds.  The long-term reference depends
 // on the decisions of earlier frames, so each location is scanned frame by
 // frame by one workgroup that keeps the previous and the reference row in
-// registers: every latent row is read once.
+// registers, with the next frames' rows in flight: every latent row is read once.
 //
 // Restoration (Dutch LIPAR page §2.D): after denoising, a pruned token takes
 // the value of the same location in the previous frame -- a forward fill along
@@ -20,6 +20,8 @@
 // written once.
 #include "common.h"
 #include "kernels.h"
+
+#include <type_traits>
 
 namespace tsa {
 
@@ -71,39 +73,42 @@ hipError_t launch_euler(void* x, int x_dtype, const uint16_t* v, long n_elems, f
 // ------------------------------------------------------- pruning mask
 
 constexpr int kLifThreads = 256;
+constexpr int kLifAhead = 4;  // frames whose rows are in flight while one is reduced
 
 template <typename T>
-struct Slice;  // one 16-byte slice of a row as fp32
+struct Slice;  // one 16-byte slice of a row, unpacked to fp32
 
 template <>
 struct Slice<uint16_t> {
   static constexpr int kVec = 8;
-  __device__ static void load(const uint16_t* p, float* f) { unpack8(*reinterpret_cast<const u32x4*>(p), f); }
+  __device__ static void unpack(const u32x4 r, float* f) { unpack8(r, f); }
 };
 
 template <>
 struct Slice<float> {
   static constexpr int kVec = 4;
-  __device__ static void load(const float* p, float* f) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(p);
-    f[0] = v[0]; f[1] = v[1]; f[2] = v[2]; f[3] = v[3];
+  __device__ static void unpack(const u32x4 r, float* f) {
+    f[0] = __uint_as_float(r[0]); f[1] = __uint_as_float(r[1]);
+    f[2] = __uint_as_float(r[2]); f[3] = __uint_as_float(r[3]);
   }
 };
 
 // Sum four values over the workgroup in a fixed order (wave butterflies, then
-// the four wave partials in wave order): deterministic.
-__device__ __forceinline__ void block_sum4(float v[4], float (*part)[4]) {
+// the four wave partials in wave order): deterministic.  part alternates between
+// two halves from call to call, so one barrier per call suffices.
+__device__ __forceinline__ void block_sum4(float v[4], float (*part)[kLifThreads / 64][4], int& parity) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int i = 0; i < 4; ++i) v[i] = wave_sum(v[i]);
+  float (*pp)[4] = part[parity];
+  parity ^= 1;
   if (lane == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) part[wave][i] = v[i];
+    for (int i = 0; i < 4; ++i) pp[wave][i] = v[i];
   }
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = (part[0][i] + part[1][i]) + (part[2][i] + part[3][i]);
-  __syncthreads();  // part is rewritten by the next call
+  for (int i = 0; i < 4; ++i) v[i] = (pp[0][i] + pp[1][i]) + (pp[2][i] + pp[3][i]);
 }
 
 __device__ __forceinline__ float l1_score(float num, float den, int relative) {
@@ -112,7 +117,9 @@ __device__ __forceinline__ float l1_score(float num, float den, int relative) {
   return num / den;
 }
 
-// One workgroup per spatial location; CPT 16-byte slices per thread and row.
+// One workgroup per spatial location; CPT 16-byte slices per thread and row.  The
+// rows of the next kLifAhead frames stay in flight (raw, in a register ring) while
+// the current one is reduced.
 template <typename T, int CPT>
 __global__ __launch_bounds__(kLifThreads) void lif_mask_kernel(const T* __restrict__ x, long frames, long hw,
                                                                long dim, int relative, float tau_s,
@@ -120,24 +127,29 @@ __global__ __launch_bounds__(kLifThreads) void lif_mask_kernel(const T* __restri
                                                                float* __restrict__ short_out,
                                                                float* __restrict__ long_out) {
   constexpr int V = Slice<T>::kVec;
-  __shared__ float part[kLifThreads / 64][4];
+  __shared__ float part[2][kLifThreads / 64][4];
   const long loc = blockIdx.x;
   const long n_sl = dim / V;
-  float prev[CPT][V], ref[CPT][V], cur[CPT][V];
-  auto load_row = [&](float (*dst)[V], long f) {
+  auto load_raw = [&](u32x4 (&dst)[CPT], long f) {
     const T* row = x + (f * hw + loc) * dim;
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
       const long sl = threadIdx.x + static_cast<long>(kLifThreads) * j;
-      if (sl < n_sl) {
-        Slice<T>::load(row + sl * V, dst[j]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < V; ++e) dst[j][e] = 0.f;
-      }
+      dst[j] = sl < n_sl ? *reinterpret_cast<const u32x4*>(row + sl * V) : u32x4{0u, 0u, 0u, 0u};
     }
   };
-  load_row(prev, 0);
+  auto unpack_row = [&](const u32x4 (&r)[CPT], float (*dst)[V]) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) Slice<T>::unpack(r[j], dst[j]);
+  };
+  float prev[CPT][V], ref[CPT][V], cur[CPT][V];
+  u32x4 ring[kLifAhead][CPT];
+  load_raw(ring[0], 0);
+#pragma unroll
+  for (int p = 1; p < kLifAhead; ++p)
+    if (p < frames) load_raw(ring[p], p);
+  unpack_row(ring[0], prev);
+  if (kLifAhead < frames) load_raw(ring[0], kLifAhead);
 #pragma unroll
   for (int j = 0; j < CPT; ++j)
 #pragma unroll
@@ -147,8 +159,15 @@ __global__ __launch_bounds__(kLifThreads) void lif_mask_kernel(const T* __restri
     if (short_out) short_out[loc] = __builtin_inff();
     if (long_out) long_out[loc] = __builtin_inff();
   }
-  if (frames > 1) load_row(cur, 1);
-  for (long f = 1; f < frames; ++f) {
+  int parity = 0;
+  // Frame f's row lives in ring slot f % kLifAhead; the slot is a compile-time
+  // index (the frame loop is unrolled by kLifAhead), so no register is copied
+  // while its load may still be in flight.
+  auto step = [&](long f, auto slot_c) {
+    constexpr int slot = decltype(slot_c)::value;
+    unpack_row(ring[slot], cur);
+    // the slot is free again: fetch the frame kLifAhead ahead into it
+    if (f + kLifAhead < frames) load_raw(ring[slot], f + kLifAhead);
     float acc[4] = {0.f, 0.f, 0.f, 0.f};  // short num, short den, long num, long den
 #pragma unroll
     for (int j = 0; j < CPT; ++j)
@@ -159,10 +178,7 @@ __global__ __launch_bounds__(kLifThreads) void lif_mask_kernel(const T* __restri
         acc[2] += fabsf(cur[j][e] - ref[j][e]);
         acc[3] += fabsf(ref[j][e]);
       }
-    // the next frame's row is in flight while this one is reduced
-    float nxt[CPT][V];
-    if (f + 1 < frames) load_row(nxt, f + 1);
-    block_sum4(acc, part);
+    block_sum4(acc, part, parity);
     const float ss = l1_score(acc[0], acc[1], relative);
     const float ls = l1_score(acc[2], acc[3], relative);
     const bool keep = !((ss < tau_s) && (ls < tau_l));
@@ -178,9 +194,23 @@ __global__ __launch_bounds__(kLifThreads) void lif_mask_kernel(const T* __restri
       for (int e = 0; e < V; ++e) {
         if (keep) ref[j][e] = cur[j][e];
         prev[j][e] = cur[j][e];
-        if (f + 1 < frames) cur[j][e] = nxt[j][e];
       }
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
+  static_assert(kLifAhead == 4, "the unrolled frame loop below has four slots");
+  long f = 1;
+  for (; f + 3 < frames; f += 4) {
+    step(f, S1{});
+    step(f + 1, S2{});
+    step(f + 2, S3{});
+    step(f + 3, S0{});
   }
+  if (f < frames) step(f, S1{});
+  if (f + 1 < frames) step(f + 1, S2{});
+  if (f + 2 < frames) step(f + 2, S3{});
 }
 
 template <typename T>
