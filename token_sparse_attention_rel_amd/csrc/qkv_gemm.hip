@@ -22,26 +22,38 @@
 // 16-byte LDS reads feed eight MFMAs, and each staged K slice is shared by 256
 // columns and 256 tokens.  Two LDS buffers (144 KB, one workgroup per CU, one
 // barrier per K step); the registers prefetch the K step after next while the
-// current one is multiplied.  bf16 rows (and the recovery noise) arrive through
+// current one is multiplied.  Grids of fewer than four such tiles per CU use
+// 128 x 128 tiles on 4 waves instead (two workgroups per CU).  bf16 rows (and the recovery noise) arrive through
 // range-checked buffer loads (invalid rows read as zeros, no per-step selects).
 #include "common.h"
 #include "kernels.h"
 
 namespace tsa {
 
-constexpr int kGemmBM = 256;  // output features per block
-constexpr int kGemmBN = 256;  // tokens per block
 constexpr int kGemmBK = 64;
-constexpr int kGemmThreads = 512;
-constexpr int kGemmWavesT = 2;                       // waves along tokens (4 along features)
-constexpr int kWaveBF = 2;                           // 32-feature MFMA blocks per wave
-constexpr int kWaveBT = 4;                           // 32-token MFMA blocks per wave
-constexpr int kLoadRows = kGemmThreads / 8;          // tile rows staged per load round
-constexpr int kLoadW = kGemmBM / kLoadRows;          // 16-byte W chunks per thread and K step
-constexpr int kLoadA = kGemmBN / kLoadRows;          // 16-byte A chunks per thread and K step
-static_assert((kGemmThreads / 64) / kGemmWavesT * kWaveBF * 32 == kGemmBM, "feature tiling");
-static_assert(kGemmWavesT * kWaveBT * 32 == kGemmBN, "token tiling");
 constexpr int kGemmLD = kGemmBK + 8;  // LDS row stride (elements): 144 B, conflict-free 16-byte reads
+
+// Workgroup tile: WF x WT waves, each BF x BT MFMA blocks of 32 x 32 (features x tokens).
+template <int WF, int WT, int BF, int BT, int MIN_BLOCKS>
+struct GemmTile {
+  static constexpr int kWavesT = WT;
+  static constexpr int kBF = BF;                      // 32-feature MFMA blocks per wave
+  static constexpr int kBT = BT;                      // 32-token MFMA blocks per wave
+  static constexpr int kThreads = 64 * WF * WT;
+  static constexpr int kBM = WF * BF * 32;            // output features per block
+  static constexpr int kBN = WT * BT * 32;            // tokens per block
+  static constexpr int kLoadRows = kThreads / 8;      // tile rows staged per load round
+  static constexpr int kLoadW = kBM / kLoadRows;      // 16-byte W chunks per thread and K step
+  static constexpr int kLoadA = kBN / kLoadRows;      // 16-byte A chunks per thread and K step
+  static constexpr int kMinBlocks = MIN_BLOCKS;       // resident workgroups per CU
+};
+// 256 x 256 on 8 waves of 64 x 128 (144 KB of LDS, one workgroup per CU) for grids that
+// fill the chip several times; 128 x 128 on 4 waves of 64 x 64 (72 KB, two per CU) for
+// smaller ones, where the large tile's last wave of workgroups would leave CUs idle.
+using TileLarge = GemmTile<4, 2, 2, 4, 1>;
+using TileSmall = GemmTile<2, 2, 2, 2, 2>;
+// The large tile is used from this many workgroups on (four per CU of a 256-CU chip).
+constexpr long kLargeTileMinBlocks = 1024;
 
 enum { kSrcBf16 = 0, kSrcF32 = 1, kSrcRecover = 2 };
 
@@ -107,8 +119,11 @@ constexpr int kOutOfRange = 0x7FFFFFF0;
 // time on one XCD then share few W panels and few token tiles in its L2.
 constexpr int kTokGroup = 4;
 
-template <int SRC>
-__global__ __launch_bounds__(kGemmThreads, 1) void qkv_gemm_kernel(GemmArgs a) {
+template <int SRC, typename TL>
+__global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void qkv_gemm_kernel(GemmArgs a) {
+  constexpr int kGemmBM = TL::kBM, kGemmBN = TL::kBN, kGemmWavesT = TL::kWavesT;
+  constexpr int kWaveBF = TL::kBF, kWaveBT = TL::kBT;
+  constexpr int kLoadRows = TL::kLoadRows, kLoadW = TL::kLoadW, kLoadA = TL::kLoadA;
   __shared__ __align__(16) uint16_t ws[2][kGemmBM * kGemmLD];
   __shared__ __align__(16) uint16_t as[2][kGemmBN * kGemmLD];
 
@@ -211,7 +226,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void qkv_gemm_kernel(GemmArgs a) {
       *reinterpret_cast<u32x4*>(&as[buf][(lrow + kLoadRows * j) * kGemmLD + lcol]) = a_chunk(j);
   };
 
-  const int wc = wave / kGemmWavesT;  // feature quarter of the block
+  const int wc = wave / kGemmWavesT;  // feature slice of the block
   const int wt = wave % kGemmWavesT;  // token half of the block
   f32x16 acc[kWaveBF][kWaveBT];
 #pragma unroll
@@ -298,6 +313,18 @@ __global__ __launch_bounds__(kGemmThreads, 1) void qkv_gemm_kernel(GemmArgs a) {
   }
 }
 
+template <typename TL>
+void launch_tile(const GemmArgs& a, const RowSource& src, long n, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((a.ncols + TL::kBM - 1) / TL::kBM * ((n + TL::kBN - 1) / TL::kBN)));
+  if (src.eps) {
+    hipLaunchKernelGGL((qkv_gemm_kernel<kSrcRecover, TL>), grid, dim3(TL::kThreads), 0, s, a);
+  } else if (src.x_dtype == kDtypeF32) {
+    hipLaunchKernelGGL((qkv_gemm_kernel<kSrcF32, TL>), grid, dim3(TL::kThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((qkv_gemm_kernel<kSrcBf16, TL>), grid, dim3(TL::kThreads), 0, s, a);
+  }
+}
+
 hipError_t launch_qkv(const RowSource& src, long n, long dim, const uint16_t* w_qkv,
                       const QkvOut& out, const RopeSpec& rope, hipStream_t s) {
   GemmArgs a;
@@ -325,15 +352,12 @@ hipError_t launch_qkv(const RowSource& src, long n, long dim, const uint16_t* w_
     a.rope_w = rope.width;
     a.rope_log2_base = rope.log2_base;
   }
-  const dim3 grid(static_cast<unsigned>((a.ncols + kGemmBM - 1) / kGemmBM *
-                                        ((n + kGemmBN - 1) / kGemmBN)));
-  if (src.eps) {
-    hipLaunchKernelGGL(qkv_gemm_kernel<kSrcRecover>, grid, dim3(kGemmThreads), 0, s, a);
-  } else if (src.x_dtype == kDtypeF32) {
-    hipLaunchKernelGGL(qkv_gemm_kernel<kSrcF32>, grid, dim3(kGemmThreads), 0, s, a);
-  } else {
-    hipLaunchKernelGGL(qkv_gemm_kernel<kSrcBf16>, grid, dim3(kGemmThreads), 0, s, a);
-  }
+  const long tiles_large =
+      (a.ncols + TileLarge::kBM - 1) / TileLarge::kBM * ((n + TileLarge::kBN - 1) / TileLarge::kBN);
+  if (tiles_large >= kLargeTileMinBlocks)
+    launch_tile<TileLarge>(a, src, n, s);
+  else
+    launch_tile<TileSmall>(a, src, n, s);
   return hipGetLastError();
 }
 
