@@ -336,6 +336,55 @@ def test_qkv_matches_oracle(n_x, m, dim, src):
     assert torch.equal(kch[rows], k.cpu()) and torch.equal(vch[rows], v.cpu())
 
 
+@pytest.mark.parametrize("src", ["bf16", "recover", "f32"])
+def test_qkv_large_tile_sampled(src):
+    """A grid of at least 1024 256x256 tiles takes the large-tile kernel: checked on sampled
+    rows (two per 256-row token tile plus the ragged tail) against the oracle."""
+    t = tsa()
+    n_x, m, dim = 9000, 7461, 3072  # 30 token tiles x 36 feature tiles
+    g = torch.Generator().manual_seed(len(src))
+    x = torch.randn(n_x, dim, generator=g)
+    x = x if src == "f32" else x.to(torch.bfloat16)
+    w = (torch.randn(3 * dim, dim, generator=g) / math.sqrt(dim)).to(torch.bfloat16)
+    rows = np.sort(np.random.default_rng(5).choice(n_x, m, replace=False)).astype(np.int32)
+    rd = G.dev(torch.from_numpy(rows))
+    q = torch.empty(m, dim, dtype=torch.bfloat16, device="cuda")
+    k = torch.empty_like(q)
+    v = torch.empty_like(q)
+    off, sigma = 900, 0.6
+    eps = _randn_bf16(g, n_x, dim) if src == "recover" else None
+    t.qkv_active(G.dev(x), rd, m, G.dev(w), q_out=q, k_out=k, v_out=v,
+                 eps=None if eps is None else G.dev(eps), src_row_offset=off, sigma=sigma)
+    rng = np.random.default_rng(6)
+    sample = np.unique(np.concatenate([np.arange(0, m, 256)[:, None] + rng.integers(0, 256, (m // 256 + 1, 2)),
+                                       np.arange(m - 5, m)[:, None]], axis=None))
+    sample = sample[sample < m]
+    if src == "recover":
+        a_rows = ref.recover_rows(G.host64(x), G.host64(eps), rows[sample], off, sigma)
+    else:
+        a_rows = G.host64(x)[rows[sample]]
+    w64 = G.host64(w)
+    want = ref.project(a_rows, w64)
+    for name, got in (("q", q), ("k", k), ("v", v)):
+        gh = G.host64(got)[sample]
+        if src == "recover":
+            G.assert_close(gh, want[name], f"large tile {src} {name}")
+        else:
+            part = "qkv".index(name)
+            wp = np.abs(w64[part * dim:(part + 1) * dim])
+            G.assert_projection_close(gh, want[name], np.abs(ref.round_bf16(a_rows)) @ wp.T, dim,
+                                      f"large tile {src} {name}")
+    # K/V into cache rows: the same values, other rows untouched
+    kc = torch.zeros(n_x, dim, dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    t.qkv_active(G.dev(x), rd, m, G.dev(w), k_out=kc, v_out=vc, out_is_cache=True, n_cache=n_x,
+                 eps=None if eps is None else G.dev(eps), src_row_offset=off, sigma=sigma)
+    others = torch.from_numpy(np.setdiff1d(np.arange(n_x), rows)).cuda()
+    rl = rd.long()
+    assert torch.equal(kc[rl], k) and torch.equal(vc[rl], v)
+    assert not kc[others].any() and not vc[others].any()
+
+
 # --------------------------------------------------------------- attention
 
 @pytest.mark.parametrize("n_q,n_kv,heads,hd", [(1, 1, 1, 64), (37, 53, 3, 64), (128, 64, 2, 128),
