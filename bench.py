@@ -36,6 +36,8 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 METRIC = "pruned-attn layer TFLOP/s + tokens/s at N=32760, 30% active; % MFMA peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_wan13b_traffic.txt")
+CLOCK_FILE = os.path.join(ROOT, "profiles", "attention_wan13b_clock.txt")
+SPEC_SCLK_GHZ = 2.4
 ATTN_SRC = os.path.join(ROOT, "token_sparse_attention_rel_amd", "csrc", "attention.hip")
 
 
@@ -85,13 +87,13 @@ def _src_hash(path):
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def attention_traffic():
-    """HBM bytes per attention launch from the committed rocprofv3 counter summary,
-    or None when it is missing or the kernel source changed since it was taken."""
-    if not os.path.exists(TRAFFIC_FILE):
+def _profile_value(path, key):
+    """A value from a committed rocprofv3 summary of the attention kernel, or None when the
+    summary is missing or the kernel source changed since it was taken."""
+    if not os.path.exists(path):
         return None
     vals = {}
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         for line in f:
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
@@ -99,9 +101,19 @@ def attention_traffic():
     try:
         if vals.get("kernel_source_sha256") != _src_hash(ATTN_SRC):
             return None
-        return float(vals["hbm_bytes_per_launch"])
+        return float(vals[key])
     except (KeyError, ValueError):
         return None
+
+
+def attention_traffic():
+    """HBM bytes per attention launch (FETCH_SIZE + WRITE_SIZE counter summary)."""
+    return _profile_value(TRAFFIC_FILE, "hbm_bytes_per_launch")
+
+
+def attention_sclk():
+    """Median shader clock (GHz) during the attention kernel (GRBM_GUI_ACTIVE summary)."""
+    return _profile_value(CLOCK_FILE, "sclk_ghz_median")
 
 
 def cpu_baseline(cfg, inp, n_sample):
@@ -300,6 +312,8 @@ def bench_step(args, torch, tsa, cfg):
 
     hbm = None if args.no_hbm else hbm_kernels(tsa, torch, cfg, layer, xc, xp)
     achieved = flops / (t_att_mean * 1e-3) / 1e12
+    # the clock summary covers the wan13b attention kernel only
+    sclk = attention_sclk() if cfg.name == "wan13b" else None
     rec = {
         "metric": METRIC if cfg.name == "wan13b" else f"pruned-attn layer TFLOP/s + tokens/s ({cfg.name})",
         "value": round(flops / (ms_step * 1e-3) / 1e12, 3),
@@ -350,6 +364,10 @@ def bench_step(args, torch, tsa, cfg):
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": attention_traffic(),
             "algorithmic_flop_per_launch": flops,
+            # the shader clock the profiled attention kernel ran at (power-limited under full
+            # MFMA load) and the fraction of the peak at that clock, next to the spec-clock frac
+            "sclk_ghz_profiled": sclk,
+            "frac_at_profiled_sclk": None if sclk is None else round(achieved / (PEAK_BF16_TFLOPS * sclk / SPEC_SCLK_GHZ), 4),
             "launch_ms_mean_events": round(t_att_mean, 5),
         },
     }

@@ -3,7 +3,8 @@
 Usage (repository root, after the GPU runs listed in each summary wrote gpurun_out/):
     python profiles/make_summaries.py gpurun_out
 Reads <dir>/prof_trace/run_kernel_trace.csv + run_kernel_stats.csv + prof_trace.log (the
-bench JSON line printed under the profiler), and <dir>/pmc_{fetch,write,copy_fetch,copy_write}.
+bench JSON line printed under the profiler), <dir>/pmc_{fetch,write,copy_fetch,copy_write} and
+<dir>/pmc_clock.
 """
 
 from __future__ import annotations
@@ -104,6 +105,47 @@ def traffic_summary(d):
     return "\n".join(out) + "\n"
 
 
+def clock_summary(d):
+    """Shader clock and MFMA activity of the attention kernel from one counter run."""
+    f = glob.glob(os.path.join(d, "pmc_clock", "*counter_collection.csv"))[0]
+    per = collections.defaultdict(dict)
+    for r in csv.DictReader(open(f)):
+        if ATTN in _short(r["Kernel_Name"]):
+            e = per[r["Dispatch_Id"]]
+            e[r["Counter_Name"]] = float(r["Counter_Value"])
+            e["ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    rows = [e for e in per.values() if "GRBM_GUI_ACTIVE" in e]
+    src = hashlib.sha256(open(os.path.join(ROOT, "token_sparse_attention_rel_amd", "csrc", "attention.hip"), "rb").read()).hexdigest()
+    out = [
+        "# Shader clock and MFMA activity of the attention kernel, wan13b pruned layer step",
+        "# command (repository root, one MI355X):",
+        "#   timeout -s KILL 120 rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_WAVES "
+        "--output-format csv -d gpurun_out/pmc_clock -o run -- python3 bench.py --steps 3 --warmup 1 "
+        "--no-cpu-baseline --no-dense --no-hbm",
+        "# summary written by: python profiles/make_summaries.py gpurun_out",
+        "# GRBM_GUI_ACTIVE counts busy GPU cycles on each of the 8 XCDs (summed): cycles = value / 8;",
+        "# sclk = cycles / kernel duration.  MFMA utilisation at that clock = algorithmic FLOP /",
+        "# (duration x sclk x 4096 FLOP/clk/CU x 256 CUs); SQ_VALU_MFMA_BUSY_CYCLES per SIMD-cycle agrees.",
+        "",
+        f"{'dispatch_us':>12s} {'sclk_GHz':>9s} {'util_at_sclk':>13s} {'MFMA_busy_per_SIMD':>19s} {'SQ_WAVES':>9s}",
+    ]
+    sclks, utils = [], []
+    for e in rows:
+        cyc = e["GRBM_GUI_ACTIVE"] / 8.0
+        sclk = cyc / e["ns"]
+        util = FLOP / (e["ns"] * 1e-9 * sclk * 1e9 * 4096 * 256)
+        sclks.append(sclk)
+        utils.append(util)
+        mb = e.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (cyc * 1024)  # per SIMD (4 per CU)
+        out.append(f"{e['ns'] / 1e3:12.1f} {sclk:9.3f} {util:13.3f} {mb:19.3f} {e.get('SQ_WAVES', 0):9.0f}")
+    sclks.sort()
+    utils.sort()
+    med = sclks[len(sclks) // 2]
+    out += ["", f"kernel: {ATTN}", f"kernel_source_sha256: {src}", f"sclk_ghz_median: {med:.3f}",
+            f"mfma_util_at_sclk_median: {utils[len(utils) // 2]:.3f}"]
+    return "\n".join(out) + "\n"
+
+
 def stats_summary(d, sub, title, command):
     """Per-kernel statistics of one rocprofv3 --kernel-trace --stats run."""
     stats = list(csv.DictReader(open(os.path.join(d, sub, "run_kernel_stats.csv"))))
@@ -137,6 +179,8 @@ def main(argv):
     here = os.path.dirname(os.path.abspath(__file__))
     open(os.path.join(here, "layer_step_wan13b_kernel_trace.txt"), "w").write(trace_summary(d))
     open(os.path.join(here, "attention_wan13b_traffic.txt"), "w").write(traffic_summary(d))
+    if glob.glob(os.path.join(d, "pmc_clock", "*counter_collection.csv")):
+        open(os.path.join(here, "attention_wan13b_clock.txt"), "w").write(clock_summary(d))
     for sub, fname, title, cmd in EXTRA:
         if os.path.exists(os.path.join(d, sub, "run_kernel_stats.csv")):
             open(os.path.join(here, fname), "w").write(stats_summary(d, sub, title, cmd))
