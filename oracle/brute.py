@@ -239,3 +239,41 @@ def attention_frame_causal(q, k, v, heads, q_tokens, frame_tokens, scale=None):
             for u in range(d):
                 out[i][c0 + u] = math.fsum(pj * v[j][c0 + u] for pj, j in zip(p, keys)) / z
     return out
+
+
+def reuse(v_rows, heads, height, width, thetas):
+    """Timeripple partial-score reuse, token by token: for each axis (time, height, width) the
+    neighbour one step back, the relative RMS difference over the channels of the two groups
+    that axis does not rotate, the first axis (in that order, not the group's own) whose
+    difference is below its threshold gives each channel group its source; the group's
+    channels are copied from the source's already resolved vector.  Returns (src, eff)."""
+    n = len(v_rows)
+    dim = len(v_rows[0])
+    d = dim // heads
+    g = 2 * (d // 6)
+    bounds = [(0, d - 2 * g), (d - 2 * g, d - g), (d - g, d)]
+    hw = height * width
+    eff = [list(r) for r in v_rows]
+    src = [[[t] * 3 for _ in range(heads)] for t in range(n)]
+    for t in range(n):
+        f, y, x = t // hw, (t // width) % height, t % width
+        nbs = [t - hw if f > 0 else None, t - width if y > 0 else None, t - 1 if x > 0 else None]
+        for h in range(heads):
+            deltas = []
+            for a in range(3):
+                j = nbs[a]
+                if j is None:
+                    deltas.append(math.inf)
+                    continue
+                chans = [h * d + c for gi, (s, e) in enumerate(bounds) if gi != a for c in range(s, e)]
+                num = math.sqrt(math.fsum((v_rows[t][c] - v_rows[j][c]) ** 2 for c in chans))
+                den = math.sqrt(math.fsum(v_rows[t][c] ** 2 for c in chans))
+                deltas.append((0.0 if num == 0 else math.inf) if den == 0 else num / den)
+            for gi, (s, e) in enumerate(bounds):
+                for a in range(3):
+                    if a != gi and deltas[a] < thetas[a]:
+                        src[t][h][gi] = nbs[a]
+                        for c in range(h * d + s, h * d + e):
+                            eff[t][c] = eff[nbs[a]][c]
+                        break
+    return src, eff

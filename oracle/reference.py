@@ -510,3 +510,111 @@ def attention_frame_causal(q, k, v, heads: int, q_tokens, frame_tokens: int, sca
         out[rows] = o
         lse[:, rows] = l
     return (out, lse) if return_lse else out
+
+
+# ------------------------------------------ f4: Timeripple partial-score reuse
+
+# Axis order of the reuse checks and of the channel groups: time (frames), height (rows),
+# width (columns) -- the order of rope_split.
+REUSE_AXES = ("t", "y", "x")
+
+
+def reuse_groups(head_dim: int) -> list:
+    """Channel ranges [start, end) of the time / height / width groups of one head: the
+    rotary groups of the Timeripple page (Metodología §1, structured encoding)."""
+    d_t, d_y, d_x = rope_split(head_dim)
+    return [(0, d_t), (d_t, d_t + d_y), (d_t + d_y, head_dim)]
+
+
+def axis_neighbors(n_tokens: int, height: int, width: int) -> np.ndarray:
+    """[3, n]: the token one step back along time / height / width (frame-major layout):
+    same location one frame earlier, one row up, one column left; -1 where there is none."""
+    t = np.arange(n_tokens, dtype=np.int64)
+    f, y, x = token_position(t, height, width)
+    nb = np.full((3, n_tokens), -1, dtype=np.int64)
+    nb[0] = np.where(f > 0, t - height * width, -1)
+    nb[1] = np.where(y > 0, t - width, -1)
+    nb[2] = np.where(x > 0, t - 1, -1)
+    return nb
+
+
+def reuse_deltas(v, heads: int, height: int, width: int) -> np.ndarray:
+    """Timeripple page, Metodología §2 (similarity checks along the time, x and y axes):
+    for token n, head h and axis a, the relative RMS difference between the token and its
+    neighbour along a over C_a, the channels of the two groups that axis a does not rotate
+    (moving along a leaves their rotary phase unchanged, Metodología §1):
+        delta[n, h, a] = ||v[n, h, C_a] - v[nb_a(n), h, C_a]||_2 / ||v[n, h, C_a]||_2
+    (0/0 -> 0, x/0 -> inf); +inf without a neighbour.  Float64."""
+    v = np.asarray(v, dtype=np.float64)
+    n, dim = v.shape
+    d = dim // heads
+    groups = reuse_groups(d)
+    nb = axis_neighbors(n, height, width)
+    out = np.full((n, heads, 3), np.inf)
+    for a in range(3):
+        chans = np.concatenate([np.arange(s, e) for g, (s, e) in enumerate(groups) if g != a])
+        has = nb[a] >= 0
+        rows = np.flatnonzero(has)
+        for h in range(heads):
+            cols = h * d + chans
+            own = v[np.ix_(rows, cols)]
+            diff = own - v[np.ix_(nb[a, rows], cols)]
+            num = np.sqrt((diff * diff).sum(1))
+            den = np.sqrt((own * own).sum(1))
+            with np.errstate(divide="ignore", invalid="ignore"):
+                out[rows, h, a] = np.where(den == 0, np.where(num == 0, 0.0, np.inf), num / den)
+    return out
+
+
+def reuse_sources(deltas, thetas, height: int, width: int) -> np.ndarray:
+    """Reuse decision (Metodología §2): a token is reusable along axis a when its delta is
+    below theta_a (strictly); any reusable axis suffices.  Channel group g of token n, head h
+    then takes its partial scores from the neighbour along the first reusable axis a != g in
+    the order time, height, width; otherwise from the token itself.  Returns
+    src[n, h, g] (a token index, = n when computed)."""
+    deltas = np.asarray(deltas, dtype=np.float64)
+    n, heads, _ = deltas.shape
+    nb = axis_neighbors(n, height, width)
+    src = np.broadcast_to(np.arange(n, dtype=np.int64)[:, None, None], (n, heads, 3)).copy()
+    for g in range(3):
+        decided = np.zeros((n, heads), dtype=bool)
+        for a in range(3):
+            if a == g:
+                continue
+            ok = (deltas[:, :, a] < float(thetas[a])) & ~decided
+            src[:, :, g] = np.where(ok, nb[a][:, None], src[:, :, g])
+            decided |= ok
+    return src
+
+
+def reuse_effective(v, src, heads: int) -> np.ndarray:
+    """Aggregation (Metodología §2): the partial scores of group g of token n are the
+    neighbour's own (computed or themselves reused), i.e. the group's channels of the
+    source token's effective vector; sources precede their tokens, so one pass in token
+    order resolves every chain.  Reusing the partial score q_g . k_g of a token is the same
+    as taking its group-g channels from the source, so the attention map is that of the
+    effective vectors."""
+    v = np.asarray(v, dtype=np.float64)
+    n, dim = v.shape
+    d = dim // heads
+    groups = reuse_groups(d)
+    eff = v.copy()
+    for t in range(n):
+        for h in range(heads):
+            for g, (s, e) in enumerate(groups):
+                j = int(src[t, h, g])
+                if j != t:
+                    eff[t, h * d + s:h * d + e] = eff[j, h * d + s:h * d + e]
+    return eff
+
+
+def timeripple_attention(q, k, v, heads: int, height: int, width: int, thetas_q, thetas_k,
+                         scale: float | None = None) -> dict:
+    """Attention with Timeripple's partial-score reuse applied independently to the queries
+    and the keys of all N tokens (Metodología §2: checks for Q and K tokens); V unchanged."""
+    sq = reuse_sources(reuse_deltas(q, heads, height, width), thetas_q, height, width)
+    sk = reuse_sources(reuse_deltas(k, heads, height, width), thetas_k, height, width)
+    q_eff = reuse_effective(q, sq, heads)
+    k_eff = reuse_effective(k, sk, heads)
+    return {"src_q": sq, "src_k": sk, "q_eff": q_eff, "k_eff": k_eff,
+            "out": attention(q_eff, k_eff, v, heads, scale)}

@@ -428,3 +428,102 @@ def check_frame_causal(attention_frame_causal, attention):
     # brute force
     want = brute.attention_frame_causal(q.tolist(), k.tolist(), v.tolist(), heads, toks.tolist(), ft)
     assert np.allclose(out, np.array(want), rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------- f4: Timeripple partial-score reuse
+
+def _grid_pos(n, height, width):
+    hw = height * width
+    return [(t // hw, (t // width) % height, t % width) for t in range(n)]
+
+
+def check_reuse(reuse_deltas, reuse_sources, reuse_effective, axis_neighbors, reuse_groups, rope3d):
+    assert reuse_groups(128) == [(0, 44), (44, 86), (86, 128)]
+    assert reuse_groups(64) == [(0, 24), (24, 44), (44, 64)]
+    frames, height, width = 3, 3, 4
+    n = frames * height * width
+    nb = axis_neighbors(n, height, width)
+    for t, (f, y, x) in enumerate(_grid_pos(n, height, width)):
+        assert nb[0, t] == (t - height * width if f else -1)
+        assert nb[1, t] == (t - width if y else -1)
+        assert nb[2, t] == (t - 1 if x else -1)
+    r = rng(19)
+    heads, d = 2, 12
+    groups = reuse_groups(d)
+    v = r.standard_normal((n, heads * d))
+    v[height * width:] = v[:-height * width] + 0.05 * r.standard_normal((n - height * width, heads * d))
+    ident = np.arange(n)[:, None, None]
+    # thresholds 0: nothing is reused, the vectors are unchanged
+    s0 = reuse_sources(reuse_deltas(v, heads, height, width), (0.0, 0.0, 0.0), height, width)
+    assert np.array_equal(s0, np.broadcast_to(ident, s0.shape))
+    assert np.array_equal(reuse_effective(v, s0, heads), v)
+    # rotary vectors of one content row: moving along an axis leaves the other two groups'
+    # channels exactly equal, so every check passes at any positive threshold; the sources
+    # follow the axis order and the effective vectors equal the originals
+    u = np.repeat(r.standard_normal((1, heads * d)), n, axis=0)
+    rv = rope3d(u, np.arange(n), height, width, heads)
+    dr = reuse_deltas(rv, heads, height, width)
+    for t, (f, y, x) in enumerate(_grid_pos(n, height, width)):
+        for a, has in enumerate((f > 0, y > 0, x > 0)):
+            assert (dr[t, :, a] == 0.0).all() if has else np.isinf(dr[t, :, a]).all()
+    sr = reuse_sources(dr, (1e-12, 1e-12, 1e-12), height, width)
+    for t, (f, y, x) in enumerate(_grid_pos(n, height, width)):
+        back = (t - height * width if f else None, t - width if y else None, t - 1 if x else None)
+        for g in range(3):
+            want = next((back[a] for a in range(3) if a != g and back[a] is not None), t)
+            assert (sr[t, :, g] == want).all(), (t, g)
+    assert np.array_equal(reuse_effective(rv, sr, heads), rv)
+    # every check passing: chains end at the frame's first token (time group), the first token
+    # of the row in frame 0 (height group) and of the column in frame 0 (width group)
+    sinf = reuse_sources(reuse_deltas(v, heads, height, width), (np.inf,) * 3, height, width)
+    eff = reuse_effective(v, sinf, heads)
+    for t, (f, y, x) in enumerate(_grid_pos(n, height, width)):
+        roots = (f * height * width, y * width, x)
+        for h in range(heads):
+            for g, (s, e) in enumerate(groups):
+                assert np.array_equal(eff[t, h * d + s:h * d + e], v[roots[g], h * d + s:h * d + e])
+    # the threshold is strict: a relative difference of exactly 0.5 is not below 0.5
+    w2 = np.zeros((2 * 1 * 1, d))
+    w2[0, groups[1][0]] = 1.0
+    w2[1, groups[1][0]] = 2.0  # |2 - 1| / |2| = 0.5 over the height and width groups
+    d2 = reuse_deltas(w2, 1, 1, 1)
+    assert d2[1, 0, 0] == 0.5
+    assert (reuse_sources(d2, (0.5, 0.0, 0.0), 1, 1)[1, 0] == 1).all()
+    assert list(reuse_sources(d2, (0.5000001, 0.0, 0.0), 1, 1)[1, 0]) == [1, 0, 0]
+    # relative: a power-of-two rescale leaves every difference and decision unchanged
+    dv = reuse_deltas(v, heads, height, width)
+    assert np.array_equal(reuse_deltas(v * 2.0 ** 9, heads, height, width), dv)
+    th = (0.3, 1.2, 0.9)
+    sv = reuse_sources(dv, th, height, width)
+    assert np.array_equal(reuse_sources(reuse_deltas(v * 2.0 ** -7, heads, height, width), th, height, width), sv)
+    assert 0 < (sv != ident).mean() < 1
+    # brute force
+    bs, be = brute.reuse(v.tolist(), heads, height, width, th)
+    assert np.array_equal(sv, np.array(bs))
+    assert np.array_equal(reuse_effective(v, sv, heads), np.array(be))
+
+
+def check_timeripple_attention(timeripple_attention, attention, rope3d):
+    r = rng(20)
+    frames, height, width, heads, d = 2, 3, 3, 2, 12
+    n = frames * height * width
+    q = r.standard_normal((n, heads * d))
+    k = r.standard_normal((n, heads * d))
+    v = r.standard_normal((n, heads * d))
+    zero = (0.0, 0.0, 0.0)
+    # no reuse: plain attention
+    res = timeripple_attention(q, k, v, heads, height, width, zero, zero)
+    assert np.allclose(res["out"], attention(q, k, v, heads), rtol=1e-14, atol=1e-14)
+    # the output is the attention of the effective vectors, each side reused independently
+    th = (0.9, 1.3, 1.1)
+    res = timeripple_attention(q, k, v, heads, height, width, th, zero)
+    assert np.array_equal(res["k_eff"], k) and not np.array_equal(res["q_eff"], q)
+    assert np.allclose(res["out"], attention(res["q_eff"], k, v, heads), rtol=1e-14, atol=1e-14)
+    res = timeripple_attention(q, k, v, heads, height, width, zero, th)
+    assert np.array_equal(res["q_eff"], q) and not np.array_equal(res["k_eff"], k)
+    assert np.allclose(res["out"], attention(q, res["k_eff"], v, heads), rtol=1e-14, atol=1e-14)
+    # rotary keys of one content row are reproduced exactly by any reuse: output unchanged
+    kr = rope3d(np.repeat(k[:1], n, axis=0), np.arange(n), height, width, heads)
+    res = timeripple_attention(q, kr, v, heads, height, width, zero, (1e-9, 1e-9, 1e-9))
+    assert np.array_equal(res["k_eff"], kr) and (res["src_k"] != np.arange(n)[:, None, None]).any()
+    assert np.allclose(res["out"], attention(q, kr, v, heads), rtol=1e-14, atol=1e-14)

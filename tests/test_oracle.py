@@ -290,3 +290,12 @@ def test_layer_step_rope_causal_matches_brute_force():
     assert np.array_equal(res["q"], np.array(rq))
     assert np.allclose(kc, np.array(kb), rtol=0, atol=0)
     assert np.allclose(res["o_a"], np.array(o), rtol=1e-12, atol=1e-12)
+
+
+def test_reuse_pinned():
+    pins.check_reuse(ref.reuse_deltas, ref.reuse_sources, ref.reuse_effective, ref.axis_neighbors,
+                     ref.reuse_groups, ref.rope3d)
+
+
+def test_timeripple_attention_pinned():
+    pins.check_timeripple_attention(ref.timeripple_attention, ref.attention, ref.rope3d)

@@ -300,3 +300,88 @@ def _causal_shifted(shift):
 @pytest.mark.parametrize("shift", [1, -1])
 def test_frame_causal_mutations_caught(shift):
     _fails(pins.check_frame_causal, _causal_shifted(shift), ref.attention)
+
+
+# ------------------------------------------- f4: Timeripple partial-score reuse
+
+def _deltas_generic(v, heads, height, width, all_channels=False, absolute=False, neighbour_den=False,
+                    swap_xy=False):
+    v = np.asarray(v, np.float64)
+    n, dim = v.shape
+    d = dim // heads
+    groups = ref.reuse_groups(d)
+    nb = ref.axis_neighbors(n, height, width)
+    if swap_xy:
+        nb = nb[[0, 2, 1]]
+    out = np.full((n, heads, 3), np.inf)
+    for a in range(3):
+        chans = np.concatenate([np.arange(s, e) for g, (s, e) in enumerate(groups) if all_channels or g != a])
+        rows = np.flatnonzero(nb[a] >= 0)
+        for h in range(heads):
+            cols = h * d + chans
+            own = v[np.ix_(rows, cols)]
+            other = v[np.ix_(nb[a, rows], cols)]
+            num = np.sqrt(((own - other) ** 2).sum(1))
+            den = np.sqrt(((other if neighbour_den else own) ** 2).sum(1))
+            with np.errstate(divide="ignore", invalid="ignore"):
+                rel = np.where(den == 0, np.where(num == 0, 0.0, np.inf), num / den)
+            out[rows, h, a] = num if absolute else rel
+    return out
+
+
+@pytest.mark.parametrize("kw", [{"all_channels": True}, {"absolute": True}, {"neighbour_den": True},
+                                {"swap_xy": True}])
+def test_reuse_delta_mutations_caught(kw):
+    _fails(pins.check_reuse, lambda *a: _deltas_generic(*a, **kw), ref.reuse_sources, ref.reuse_effective,
+           ref.axis_neighbors, ref.reuse_groups, ref.rope3d)
+
+
+def _sources_generic(deltas, thetas, height, width, order=(0, 1, 2), every_axis=False, non_strict=False):
+    deltas = np.asarray(deltas, np.float64)
+    n, heads, _ = deltas.shape
+    nb = ref.axis_neighbors(n, height, width)
+    src = np.broadcast_to(np.arange(n)[:, None, None], (n, heads, 3)).copy()
+    for g in range(3):
+        axes = [a for a in order if a != g]
+        passes = [(deltas[:, :, a] <= thetas[a]) if non_strict else (deltas[:, :, a] < thetas[a]) for a in axes]
+        if every_axis:
+            allp = np.logical_and.reduce(passes)
+            src[:, :, g] = np.where(allp, nb[axes[0]][:, None], src[:, :, g])
+            continue
+        decided = np.zeros((n, heads), dtype=bool)
+        for a, ok in zip(axes, passes):
+            ok = ok & ~decided
+            src[:, :, g] = np.where(ok, nb[a][:, None], src[:, :, g])
+            decided |= ok
+    return src
+
+
+@pytest.mark.parametrize("kw", [{"order": (2, 1, 0)}, {"every_axis": True}, {"non_strict": True}])
+def test_reuse_source_mutations_caught(kw):
+    _fails(pins.check_reuse, ref.reuse_deltas, lambda *a: _sources_generic(*a, **kw), ref.reuse_effective,
+           ref.axis_neighbors, ref.reuse_groups, ref.rope3d)
+
+
+def _effective_from_originals(v, src, heads):
+    v = np.asarray(v, np.float64)
+    d = v.shape[1] // heads
+    eff = v.copy()
+    for t in range(v.shape[0]):
+        for h in range(heads):
+            for g, (s, e) in enumerate(ref.reuse_groups(d)):
+                j = int(src[t, h, g])
+                eff[t, h * d + s:h * d + e] = v[j, h * d + s:h * d + e]  # the source's own values, not resolved
+    return eff
+
+
+def test_reuse_effective_mutation_caught():
+    _fails(pins.check_reuse, ref.reuse_deltas, ref.reuse_sources, _effective_from_originals,
+           ref.axis_neighbors, ref.reuse_groups, ref.rope3d)
+
+
+def test_timeripple_attention_mutation_caught():
+    def keys_not_reused(q, k, v, heads, height, width, thetas_q, thetas_k, scale=None):
+        res = ref.timeripple_attention(q, k, v, heads, height, width, thetas_q, (0.0, 0.0, 0.0), scale)
+        res["src_k"] = ref.reuse_sources(ref.reuse_deltas(k, heads, height, width), thetas_k, height, width)
+        return res
+    _fails(pins.check_timeripple_attention, keys_not_reused, ref.attention, ref.rope3d)
