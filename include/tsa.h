@@ -10,6 +10,7 @@
  *           Generación Eficiente de Video", gist.science/es/paper/2605.06892
  *   [LIPAR] "Training-free Latent Inter-Frame Pruning with Attention Recovery",
  *           gist.science/es/paper/2603.05811 (and the Dutch page /nl/)
+ *   [Timeripple] "Resumen Técnico: TIMERIPPLE", gist.science/es/paper/2511.12035
  *
  * Conventions shared by every call
  *   - Pointers named *device* are device (HBM) addresses owned by the caller;
@@ -37,7 +38,7 @@
 extern "C" {
 #endif
 
-#define TSA_ABI_VERSION 4
+#define TSA_ABI_VERSION 5
 
 typedef uint16_t tsa_bf16;
 
@@ -339,6 +340,42 @@ tsa_status tsa_lif_mask(const void* x, int dtype, int64_t frames, int64_t hw, in
  */
 tsa_status tsa_restore_frames(void* buf, int dtype, const uint8_t* mask, int64_t frames, int64_t hw,
                               int64_t dim, void* stream);
+
+/* Bytes of device workspace tsa_timeripple_reuse needs: 2 * n_rows * heads * 3 * 4. */
+size_t tsa_reuse_workspace_bytes(int64_t n_rows, int heads);
+
+/*
+ * [Timeripple] Metodología §1-§2: partial attention scores of Q or K tokens
+ * reused from neighbouring tokens.  A head's channels form the rotary groups
+ * time [0, d_t), height [d_t, d_t + d_s), width [d_t + d_s, d) with
+ * d_s = 2 * (d / 6), d_t = d - 2 * d_s.  For token t (frame-major: frame
+ * t / (height*width), row (t / width) % height, column t % width), head h and
+ * axis a (0 time, 1 height, 2 width), with nb_a(t) the token one frame, row or
+ * column back:
+ *   delta[t,h,a] = ||v[t,h,C_a] - v[nb_a(t),h,C_a]||_2 / ||v[t,h,C_a]||_2
+ * over C_a = the channels of the two groups axis a does not rotate (0/0 -> 0,
+ * x/0 -> +inf; +inf when there is no neighbour), sums in fp32.  Group g of
+ * token t takes its channels from the neighbour along the first axis a != g
+ * (order time, height, width) with delta[t,h,a] < thetas[a]; from itself when
+ * there is none.  Sources are followed back to the token that keeps the group's
+ * own channels, so
+ *   v_eff[t, h, group g] = v[root(t, h, g), h, group g],
+ * and attention of (Q_eff, K_eff, V) is attention with reused partial scores.
+ *   v          device bf16 [n_rows, heads * head_dim] (Q or K, rotary positions
+ *              already applied); must not overlap v_eff.
+ *   thetas     host float[3] (time, height, width), each >= 0 or +inf, not NaN.
+ *   v_eff      device bf16 [n_rows, heads * head_dim].
+ *   src_out    device i32[n_rows, heads, 3] (the immediate source token of each
+ *              group) or NULL.
+ *   delta_out  device f32[n_rows, heads, 3] (delta per axis) or NULL.
+ *   workspace  device, at least tsa_reuse_workspace_bytes(n_rows, heads) bytes,
+ *              4-byte aligned.
+ * head_dim 64 or 128; height, width >= 1.
+ * Errors: INVALID_ARG, SHAPE, ALIGNMENT, WORKSPACE, HIP.
+ */
+tsa_status tsa_timeripple_reuse(const tsa_bf16* v, int64_t n_rows, int heads, int head_dim, int64_t height,
+                                int64_t width, const float* thetas, tsa_bf16* v_eff, int32_t* src_out,
+                                float* delta_out, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

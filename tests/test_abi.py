@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(root):
 
 
 def test_version_and_status_strings():
-    assert tsa.abi_version() == 4
+    assert tsa.abi_version() == 5
     assert tsa.status_string(0) == "ok"
     assert "shape" in tsa.status_string(B.ERR_SHAPE)
     assert tsa.status_string(99) == "unknown status"
@@ -204,3 +204,33 @@ def test_rope_and_causal_validation():
     assert fc(ft=0) == B.ERR_SHAPE
     assert fc(hd=96) == B.ERR_SHAPE
     assert fc(qt=A + 2) == B.ERR_ALIGNMENT
+
+
+def test_reuse_validation():
+    f = lib()
+    assert tsa.reuse_workspace_bytes(100, 3) == 2 * 100 * 3 * 3 * 4
+    assert tsa.reuse_workspace_bytes(0, 3) == 0
+    big = 1 << 40
+
+    def ru(th=(0.1, 0.1, 0.1), **kw):
+        t = (ctypes.c_float * 3)(*th)
+        a = dict(v=A, n=64, heads=2, hd=128, h=4, w=4, eff=A + big, src=None, delta=None, ws=A + 2 * big,
+                 wsb=2 * 64 * 2 * 3 * 4)
+        a.update(kw)
+        return f.tsa_timeripple_reuse(a["v"], a["n"], a["heads"], a["hd"], a["h"], a["w"],
+                                      ctypes.cast(t, ctypes.c_void_p), a["eff"], a["src"], a["delta"], a["ws"],
+                                      a["wsb"], None)
+    assert ru(n=0) == B.OK
+    assert ru(n=0, ws=None, wsb=0) == B.OK
+    assert ru(v=None) == B.ERR_INVALID_ARG
+    assert ru(eff=None) == B.ERR_INVALID_ARG
+    assert ru(th=(0.1, float("nan"), 0.1)) == B.ERR_INVALID_ARG
+    assert ru(th=(-0.1, 0.1, 0.1)) == B.ERR_INVALID_ARG
+    assert ru(eff=A + 64) == B.ERR_INVALID_ARG  # overlaps v
+    assert ru(hd=96) == B.ERR_SHAPE
+    assert ru(heads=0) == B.ERR_SHAPE
+    assert ru(h=0) == B.ERR_SHAPE
+    assert ru(v=U) == B.ERR_ALIGNMENT
+    assert ru(src=A + 2) == B.ERR_ALIGNMENT
+    assert ru(ws=None) == B.ERR_WORKSPACE
+    assert ru(wsb=100) == B.ERR_WORKSPACE

@@ -30,11 +30,13 @@ from ._binding import (
     qkv_active,
     qkv_active_rope,
     restore_frames,
+    reuse_workspace_bytes,
     scatter_out,
     select_active,
     select_workspace_bytes,
     sparse_query_attention,
     status_string,
+    timeripple_reuse,
     token_scores,
 )
 from .layer import PrunedAttentionLayer, hsa_active_count

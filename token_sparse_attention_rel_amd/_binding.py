@@ -52,6 +52,8 @@ _SIGNATURES = {
     "tsa_euler_update": (_int, [_vp, _int, _vp, _i64, _i64, _f32, _vp]),
     "tsa_lif_mask": (_int, [_vp, _int, _i64, _i64, _i64, _int, _f32, _f32, _vp, _vp, _vp, _vp]),
     "tsa_restore_frames": (_int, [_vp, _int, _vp, _i64, _i64, _i64, _vp]),
+    "tsa_reuse_workspace_bytes": (_size, [_i64, _int]),
+    "tsa_timeripple_reuse": (_int, [_vp, _i64, _int, _int, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _size, _vp]),
 }
 
 _lib_handle = None
@@ -242,6 +244,22 @@ def restore_frames(buf, mask, frames, hw, stream=None):
     st = lib().tsa_restore_frames(_ptr(buf), _dtype_code(buf), _ptr(mask), int(frames), int(hw),
                                   int(buf.shape[1]), _stream(stream))
     _check("tsa_restore_frames", st)
+
+
+def reuse_workspace_bytes(n_rows, heads):
+    return int(lib().tsa_reuse_workspace_bytes(int(n_rows), int(heads)))
+
+
+def timeripple_reuse(v, heads, head_dim, height, width, thetas, eff_out, workspace, *, src_out=None,
+                     delta_out=None, stream=None):
+    """Partial-score reuse on Q or K rows (tsa_timeripple_reuse); thetas = (time, height, width)."""
+    th = (ctypes.c_float * 3)(*[float(t) for t in thetas])
+    st = lib().tsa_timeripple_reuse(_ptr(v), int(v.shape[0]), int(heads), int(head_dim), int(height),
+                                    int(width), ctypes.cast(th, ctypes.c_void_p), _ptr(eff_out), _ptr(src_out),
+                                    _ptr(delta_out), _ptr(workspace),
+                                    0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                    _stream(stream))
+    _check("tsa_timeripple_reuse", st)
 
 
 def token_scores(x_cur, x_ref, scores_out, *, ref_row_offset=0, score_kind=SCORE_REL_L1, stream=None):

@@ -76,4 +76,9 @@ hipError_t launch_lif_mask(const void* x, int dtype, long frames, long hw, long 
                            float tau_l, uint8_t* mask, float* short_out, float* long_out, hipStream_t s);
 hipError_t launch_restore(void* buf, const uint8_t* mask, long frames, long hw, long row_bytes, hipStream_t s);
 
+// reuse.hip (ws_src, ws_root: n * heads * 3 int32 each)
+hipError_t launch_reuse(const uint16_t* v, long n, int heads, int head_dim, long height, long width,
+                        const float theta[3], uint16_t* eff, int* src_out, float* delta_out, int* ws_src,
+                        int* ws_root, hipStream_t s);
+
 }  // namespace tsa

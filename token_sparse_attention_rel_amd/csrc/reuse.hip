@@ -1,0 +1,188 @@
+// f4: Timeripple partial-score reuse on Q or K (Timeripple page, Metodología §1-§2).
+//
+// A head's channels form the three rotary groups time / height / width (sizes
+// d - 4*(d/6), 2*(d/6), 2*(d/6)).  Moving along one axis leaves the rotary phase
+// of the other two groups unchanged, so those channels of neighbouring tokens
+// tend to agree.  For every token, head and axis:
+//
+//   delta[n,h,a] = ||v[n,h,C_a] - v[nb_a(n),h,C_a]|| / ||v[n,h,C_a]||
+//
+// over C_a = the channels of the two groups axis a does not rotate, nb_a the
+// token one step back along a (one frame, row or column); no neighbour: +inf.
+// Group g of the token then reuses the partial scores of the neighbour along the
+// first axis a != g (order time, height, width) whose delta is below theta_a,
+// which is the same as taking the group's channels from that neighbour's own
+// (resolved) vector.  The attention of the resulting effective vectors is the
+// attention with reused partial scores.
+//
+// Three kernels, each a flat pass:
+//   delta_src: L = d/8 lanes per (token, head), 16-byte slices, shuffle sums;
+//   resolve:   one thread per (token, head, group) follows the sources back to the
+//              token that computes the group itself (every step moves back along
+//              an axis, so a chain is at most frame + row + column steps long);
+//   copy:      one thread per 4-byte channel pair writes the effective row.
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace tsa {
+
+struct ReuseGeom {
+  long n;
+  int heads;
+  long hw;     // tokens per frame
+  long width;  // tokens per row
+  int d_t;     // channels of the time group; the height group follows with d_s, then width
+  int d_s;
+};
+
+__device__ __forceinline__ int channel_group(const ReuseGeom& g, int c) {
+  return c < g.d_t ? 0 : (c < g.d_t + g.d_s ? 1 : 2);
+}
+
+// The token one step back along axis a (0 time, 1 height, 2 width), or -1.
+__device__ __forceinline__ long axis_back(const ReuseGeom& g, long t, int a) {
+  if (a == 0) return t >= g.hw ? t - g.hw : -1;
+  const long in_frame = t % g.hw;
+  if (a == 1) return in_frame >= g.width ? t - g.width : -1;
+  return in_frame % g.width ? t - 1 : -1;
+}
+
+template <int HD>
+__global__ __launch_bounds__(256) void reuse_delta_src_kernel(const uint16_t* __restrict__ v, ReuseGeom geo,
+                                                              float th0, float th1, float th2,
+                                                              int* __restrict__ src, int* __restrict__ src_copy,
+                                                              float* __restrict__ delta_out) {
+  constexpr int L = HD / 8;  // lanes per (token, head), 8 channels each
+  const long pair = (static_cast<long>(blockIdx.x) * 256 + threadIdx.x) / L;
+  const int sub = threadIdx.x % L;
+  const long n_pairs = geo.n * geo.heads;
+  const bool live = pair < n_pairs;
+  const long t = live ? pair / geo.heads : 0;
+  const int h = static_cast<int>(pair % geo.heads);
+  const long dim = static_cast<long>(geo.heads) * HD;
+  const long col = static_cast<long>(h) * HD + 8 * sub;
+
+  float own[8];
+  unpack8(*reinterpret_cast<const u32x4*>(v + t * dim + col), own);
+  int grp[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) grp[e] = channel_group(geo, 8 * sub + e);
+
+  float num[3], den[3];
+  long nb[3];
+#pragma unroll
+  for (int a = 0; a < 3; ++a) {
+    nb[a] = live ? axis_back(geo, t, a) : -1;
+    float w[8];
+    unpack8(*reinterpret_cast<const u32x4*>(v + (nb[a] >= 0 ? nb[a] : t) * dim + col), w);
+    float s_num = 0.f, s_den = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (grp[e] != a) {
+        const float dv = own[e] - w[e];
+        s_num = fmaf(dv, dv, s_num);
+        s_den = fmaf(own[e], own[e], s_den);
+      }
+    }
+    // sum over the L lanes of this (token, head): xor butterflies inside the lane group
+#pragma unroll
+    for (int off = L / 2; off > 0; off >>= 1) {
+      s_num += __shfl_xor(s_num, off, kWave);
+      s_den += __shfl_xor(s_den, off, kWave);
+    }
+    num[a] = s_num;
+    den[a] = s_den;
+  }
+  if (!live || sub != 0) return;
+  const float theta[3] = {th0, th1, th2};
+  float delta[3];
+#pragma unroll
+  for (int a = 0; a < 3; ++a) {
+    if (nb[a] < 0)
+      delta[a] = __builtin_inff();
+    else if (den[a] == 0.f)
+      delta[a] = num[a] == 0.f ? 0.f : __builtin_inff();
+    else
+      delta[a] = sqrtf(num[a]) / sqrtf(den[a]);
+  }
+  const long base = pair * 3;
+#pragma unroll
+  for (int gi = 0; gi < 3; ++gi) {
+    long from = t;
+#pragma unroll
+    for (int a = 2; a >= 0; --a)  // the first qualifying axis in time, height, width order wins
+      if (a != gi && delta[a] < theta[a]) from = nb[a];
+    src[base + gi] = static_cast<int>(from);
+    if (src_copy) src_copy[base + gi] = static_cast<int>(from);
+    if (delta_out) delta_out[base + gi] = delta[gi];
+  }
+}
+
+// root[(t*heads + h)*3 + g] = the token whose own channels group g of token t ends up with.
+__global__ __launch_bounds__(256) void reuse_resolve_kernel(const int* __restrict__ src, long n_entries,
+                                                            int heads, int* __restrict__ root) {
+  const long i = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n_entries) return;
+  const long hg = i % (3L * heads);  // (head, group) part of the entry index
+  long s = i / (3L * heads);
+  long nx = src[i];
+  // sources strictly precede their tokens: at most s steps
+  for (long it = 0; nx != s && it <= i; ++it) {
+    s = nx;
+    nx = src[s * 3L * heads + hg];
+  }
+  root[i] = static_cast<int>(s);
+}
+
+// eff[t, h*HD + 2w .. +1] = v[root(t, h, group(2w)), same channels]
+template <int HD>
+__global__ __launch_bounds__(256) void reuse_copy_kernel(const uint32_t* __restrict__ v, const int* __restrict__ root,
+                                                         ReuseGeom geo, uint32_t* __restrict__ eff) {
+  constexpr int WPH = HD / 2;  // 4-byte channel pairs per head
+  const long i = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
+  const long words = static_cast<long>(geo.heads) * WPH;
+  if (i >= geo.n * words) return;
+  const long t = i / words;
+  const long w = i - t * words;
+  const int h = static_cast<int>(w / WPH);
+  const int g = channel_group(geo, static_cast<int>(2 * (w % WPH)));  // group bounds are even
+  const long from = root[(t * geo.heads + h) * 3 + g];
+  eff[i] = v[from * words + w];
+}
+
+hipError_t launch_reuse(const uint16_t* v, long n, int heads, int head_dim, long height, long width,
+                        const float theta[3], uint16_t* eff, int* src_out, float* delta_out, int* ws_src,
+                        int* ws_root, hipStream_t s) {
+  ReuseGeom geo;
+  geo.n = n;
+  geo.heads = heads;
+  geo.hw = height * width;
+  geo.width = width;
+  geo.d_s = 2 * (head_dim / 6);
+  geo.d_t = head_dim - 2 * geo.d_s;
+  const long pairs = n * heads;
+  if (head_dim == 128) {
+    const long threads = pairs * 16;
+    hipLaunchKernelGGL(reuse_delta_src_kernel<128>, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256),
+                       0, s, v, geo, theta[0], theta[1], theta[2], ws_src, src_out, delta_out);
+  } else {
+    const long threads = pairs * 8;
+    hipLaunchKernelGGL(reuse_delta_src_kernel<64>, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256),
+                       0, s, v, geo, theta[0], theta[1], theta[2], ws_src, src_out, delta_out);
+  }
+  const long entries = pairs * 3;
+  hipLaunchKernelGGL(reuse_resolve_kernel, dim3(static_cast<unsigned>((entries + 255) / 256)), dim3(256), 0, s,
+                     ws_src, entries, heads, ws_root);
+  const long words = n * heads * (head_dim / 2);
+  if (head_dim == 128)
+    hipLaunchKernelGGL(reuse_copy_kernel<128>, dim3(static_cast<unsigned>((words + 255) / 256)), dim3(256), 0, s,
+                       reinterpret_cast<const uint32_t*>(v), ws_root, geo, reinterpret_cast<uint32_t*>(eff));
+  else
+    hipLaunchKernelGGL(reuse_copy_kernel<64>, dim3(static_cast<unsigned>((words + 255) / 256)), dim3(256), 0, s,
+                       reinterpret_cast<const uint32_t*>(v), ws_root, geo, reinterpret_cast<uint32_t*>(eff));
+  return hipGetLastError();
+}
+
+}  // namespace tsa

@@ -327,4 +327,36 @@ tsa_status tsa_restore_frames(void* buf, int dtype, const uint8_t* mask, int64_t
   return from_hip(tsa::launch_restore(buf, mask, frames, hw, row_bytes, as_stream(stream)));
 }
 
+size_t tsa_reuse_workspace_bytes(int64_t n_rows, int heads) {
+  if (n_rows <= 0 || heads <= 0) return 0;
+  return static_cast<size_t>(2) * static_cast<size_t>(n_rows) * static_cast<size_t>(heads) * 3 * 4;
+}
+
+tsa_status tsa_timeripple_reuse(const tsa_bf16* v, int64_t n_rows, int heads, int head_dim, int64_t height,
+                                int64_t width, const float* thetas, tsa_bf16* v_eff, int32_t* src_out,
+                                float* delta_out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!v || !v_eff || !thetas) return TSA_ERR_INVALID_ARG;
+  for (int a = 0; a < 3; ++a)
+    if (isnan(thetas[a]) || thetas[a] < 0.f) return TSA_ERR_INVALID_ARG;
+  if (heads < 1 || heads > 4096 || (head_dim != 64 && head_dim != 128)) return TSA_ERR_SHAPE;
+  if (n_rows < 0 || n_rows > kMaxRows) return TSA_ERR_SHAPE;
+  if (height < 1 || width < 1 || height > kMaxRows || width > kMaxRows || height * width > kMaxRows)
+    return TSA_ERR_SHAPE;
+  // token entries (n * heads * 3) and 4-byte channel pairs are indexed with 32-bit grids
+  if (n_rows * heads * 3 > kMaxRows || n_rows * heads * (head_dim / 2) > kMaxRows * 256) return TSA_ERR_SHAPE;
+  const int64_t row_bytes = static_cast<int64_t>(heads) * head_dim * 2;
+  const uintptr_t vb = reinterpret_cast<uintptr_t>(v), eb = reinterpret_cast<uintptr_t>(v_eff);
+  const uintptr_t span = static_cast<uintptr_t>(n_rows * row_bytes);
+  if (n_rows > 0 && vb < eb + span && eb < vb + span) return TSA_ERR_INVALID_ARG;  // overlap
+  if (!aligned16(v) || !aligned16(v_eff) || (src_out && !aligned4(src_out)) || (delta_out && !aligned4(delta_out)))
+    return TSA_ERR_ALIGNMENT;
+  if (n_rows == 0) return TSA_OK;
+  if (!workspace || workspace_bytes < tsa_reuse_workspace_bytes(n_rows, heads)) return TSA_ERR_WORKSPACE;
+  if (!aligned4(workspace)) return TSA_ERR_ALIGNMENT;
+  int* ws_src = static_cast<int*>(workspace);
+  int* ws_root = ws_src + n_rows * heads * 3;
+  return from_hip(tsa::launch_reuse(v, n_rows, heads, head_dim, height, width, thetas, v_eff, src_out, delta_out,
+                                    ws_src, ws_root, as_stream(stream)));
+}
+
 }  // extern "C"
