@@ -613,6 +613,82 @@ def bench_lipar_lif(args, torch, tsa, cfg):
     }
 
 
+def bench_reuse(args, torch, tsa, cfg):
+    """Timeripple partial-score reuse (Timeripple page, Metodología §2) over a frame-correlated
+    clip: the dense pass with reuse (rotated QKV of every token, reuse on Q and K, attention of
+    the effective vectors) against the same pass without reuse, the share of partial scores
+    reused, and the reuse kernels alone against HBM."""
+    import numpy as np
+
+    from workloads import generate
+
+    dev = torch.device("cuda:0")
+    inp = generate.lipar_inputs(cfg, args.seed)
+    x = inp["x"].to(dev)
+    layer = tsa.PrunedAttentionLayer(cfg.n, cfg.dim, cfg.heads, inp["w_qkv"].to(dev), device=dev,
+                                     rope=(cfg.height, cfg.width, 10000.0))
+    th = cfg.reuse_theta
+    stream = torch.cuda.current_stream()
+    for _ in range(max(1, args.warmup // 5)):
+        layer.reuse_forward(x, th, th)
+        layer.dense_forward(x)
+    torch.cuda.synchronize()
+    reps = max(3, args.steps // 10)
+    t_pass, t_dense = EventTimer(torch, stream), EventTimer(torch, stream)
+    for _ in range(reps):
+        t_pass.start()
+        layer.reuse_forward(x, th, th)
+        t_pass.stop()
+        t_dense.start()
+        layer.dense_forward(x)
+        t_dense.stop()
+    layer.reuse_forward(x, th, th)
+    torch.cuda.synchronize()
+    # the reuse kernels alone (Q then K rows of the last pass), MALL flushed before each repetition
+    flush = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device=dev)
+    t_reuse = EventTimer(torch, stream)
+    for _ in range(20):
+        flush.max()
+        t_reuse.start()
+        tsa.timeripple_reuse(layer.q_a, cfg.heads, cfg.head_dim, cfg.height, cfg.width, th, layer._q_eff,
+                             layer._reuse_ws)
+        t_reuse.stop()
+    torch.cuda.synchronize()
+    ident = np.arange(cfg.n)[:, None]
+    d_t = cfg.head_dim - 2 * 2 * (cfg.head_dim // 6)
+    sizes = np.array([d_t, 2 * (cfg.head_dim // 6), 2 * (cfg.head_dim // 6)], dtype=np.float64)
+    reuse = {}
+    for name, src in (("q", layer.src_q), ("k", layer.src_k)):
+        sh = src.cpu().numpy()
+        used = sh != ident[:, :, None]
+        per_group = used.mean(axis=(0, 1))
+        reuse[name] = {"entries_reused": {a: round(float(per_group[i]), 4) for i, a in enumerate("tyx")},
+                       "partial_score_share_reused": round(float((per_group * sizes).sum() / sizes.sum()), 4)}
+    st, sd = stats(t_pass.times()), stats(t_dense.times())
+    fl = 4 * cfg.n * cfg.n * cfg.head_dim * cfg.heads
+    reuse_bytes = 2 * cfg.n * cfg.dim * 2 + 2 * cfg.n * cfg.heads * 3 * 4
+    return {
+        "metric": "Timeripple partial-score reuse: dense pass with reuse, effective TFLOP/s and share of "
+                  "partial scores reused",
+        "value": round(fl / (st["median"] * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "higher_is_better": True,
+        "dtype": "bf16",
+        "data": "synthetic (seeded frame-correlated clip; random-init projection weights)",
+        "config": {"workload": f"{cfg.name}: F={cfg.frames} H={cfg.height} W={cfg.width} -> N={cfg.n}, "
+                               f"D={cfg.dim}, {cfg.heads}x{cfg.head_dim}, rotary Q/K, thresholds "
+                               f"(t, y, x) = {tuple(cfg.reuse_theta)} on Q and K", "seed": args.seed},
+        "pass_ms": st,
+        "dense_pass_without_reuse_ms": sd,
+        "reuse": reuse,
+        "reuse_kernels_one_tensor": roofline_entry("hbm", reuse_bytes, stats(t_reuse.times()), "GB/s"),
+        "note": "reused partial scores are taken as effective Q/K channels; the attention kernel "
+                "computes every score, so the pass costs what the dense pass costs plus the reuse kernels",
+        "repetitions": reps,
+    }
+
+
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -631,7 +707,7 @@ def main(argv=None):
     cfg = configs.get_config(args.workload)
     torch.cuda.set_device(0)
     fn = {"step": bench_step, "hsa": bench_hsa, "hsa_loop": bench_hsa_loop, "lipar": bench_lipar,
-          "lipar_lif": bench_lipar_lif}[cfg.kind]
+          "lipar_lif": bench_lipar_lif, "reuse": bench_reuse}[cfg.kind]
     rec = fn(args, torch, tsa, cfg)
     print(json.dumps(rec), flush=True)
     return 0

@@ -172,3 +172,32 @@ def test_reuse_full_size_wan_grid():
     reused = (src != np.arange(n)[:, None, None]).mean()
     print(f"  reused (token, head, group) entries: {reused:.3f}", flush=True)
     assert 0.3 < reused < 0.8
+
+
+def test_layer_reuse_forward_scaled():
+    """The layer's dense pass with reuse: rotated QKV of every token, reuse on Q and K,
+    attention of the effective vectors, outputs in token order."""
+    from workloads import configs, generate
+    from workloads.configs import scaled
+
+    t = tsa()
+    cfg = scaled(configs.get_config("timeripple"), frames=4, height=6, width=10, dim=256, heads=2)
+    inp = generate.lipar_inputs(cfg, 0)
+    x, w = inp["x"], inp["w_qkv"]
+    rope = (cfg.height, cfg.width, 10000.0)
+    layer = t.PrunedAttentionLayer(cfg.n, cfg.dim, cfg.heads, G.dev(w), rope=rope)
+    th_q, th_k = (0.05, 0.05, 0.05), (0.05, 0.05, 0.05)
+    layer.reuse_forward(G.dev(x), th_q, th_k)
+    torch.cuda.synchronize()
+    toks = np.arange(cfg.n)
+    p = ref.project_rope(G.host64(x), toks, G.host64(w), cfg.heads, *rope)
+    src_q = layer.src_q.cpu().numpy().astype(np.int64)
+    src_k = layer.src_k.cpu().numpy().astype(np.int64)
+    assert (src_q != toks[:, None, None]).mean() > 0.2
+    # the oracle's own decisions on its Q/K agree away from the thresholds
+    own_q = ref.reuse_sources(ref.reuse_deltas(p["q"], cfg.heads, cfg.height, cfg.width), th_q, cfg.height, cfg.width)
+    print(f"  Q sources equal to the oracle's own: {(own_q == src_q).mean():.4f}", flush=True)
+    assert (own_q == src_q).mean() > 0.99
+    want = ref.attention(ref.reuse_effective(p["q"], src_q, cfg.heads), ref.reuse_effective(p["k"], src_k, cfg.heads),
+                         p["v"], cfg.heads)
+    G.assert_close(G.host64(layer.out), want, "layer pass with reuse")

@@ -184,6 +184,32 @@ class PrunedAttentionLayer:
         if k:
             self._attend(k, self.out, self.idx, rows=self.idx, stream=stream)
 
+    # ------------------------------------------------------- partial-score reuse
+
+    def reuse_forward(self, x, thetas_q, thetas_k, *, stream=None) -> None:
+        """Dense pass with Timeripple's partial-score reuse (Timeripple page, Metodología §2):
+        rotated Q/K/V of every token, each channel group of each Q and K row taken from the
+        neighbouring token whose group passes the similarity check (reuse_effective), then
+        attention of the effective Q over the effective K in token order.  Needs ``rope``."""
+        if self.rope is None:
+            raise ValueError("partial-score reuse works on the rotary channel groups: construct with rope=")
+        h, w, _ = self.rope
+        bf = torch.bfloat16
+        if getattr(self, "_q_eff", None) is None:
+            self._q_eff = torch.empty(self.n, self.dim, dtype=bf, device=self.device)
+            self._k_eff = torch.empty(self.n, self.dim, dtype=bf, device=self.device)
+            self.src_q = torch.empty(self.n, self.heads, 3, dtype=torch.int32, device=self.device)
+            self.src_k = torch.empty(self.n, self.heads, 3, dtype=torch.int32, device=self.device)
+            self._reuse_ws = torch.empty(B.reuse_workspace_bytes(self.n, self.heads), dtype=torch.uint8,
+                                         device=self.device)
+        self._qkv(x, None, self.n, q_out=self.q_a, k_out=self.k_cache, v_out=self.v_cache, stream=stream)
+        B.timeripple_reuse(self.q_a, self.heads, self.head_dim, h, w, thetas_q, self._q_eff, self._reuse_ws,
+                           src_out=self.src_q, stream=stream)
+        B.timeripple_reuse(self.k_cache, self.heads, self.head_dim, h, w, thetas_k, self._k_eff, self._reuse_ws,
+                           src_out=self.src_k, stream=stream)
+        B.sparse_query_attention(self._q_eff, self._k_eff, self.v_cache, self.n, self.heads, self.head_dim,
+                                 self.out, workspace=self.attention_workspace(self.n), stream=stream)
+
     # ------------------------------------------------------- sampling loop
 
     def dense_forward(self, x, stream=None) -> None:

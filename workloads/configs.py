@@ -38,6 +38,7 @@ class Config:
     tau_long: float = 0.0  # "lipar_lif": threshold on the L1 change against the last kept frame
     rope: bool = False  # "step": 3D rotary positions on Q and K (base 10000)
     causal: bool = False  # "step": frame-causal attention (a query sees the frames up to its own)
+    reuse_theta: tuple = ()  # "reuse": thresholds (time, height, width) of the partial-score reuse of Q and K
 
     @property
     def n(self) -> int:
@@ -49,7 +50,7 @@ class Config:
 
     @property
     def n_static(self) -> int:
-        if self.kind.startswith("lipar"):
+        if self.kind.startswith("lipar") or self.kind == "reuse":
             return self.static_pct * self.hw // 100
         return self.static_pct * self.n // 100
 
@@ -99,6 +100,11 @@ CONFIGS = {
         "hsa_loop", "hsa_loop", 21, 30, 52, 1536, 12, 128, "bf16", static_pct=70,
         steps=8, group_pcts=(25, 25, 50), group_budgets=(8, 4, 2), window=1,
     ),
+    # Timeripple partial-score reuse over a 21x30x52 clip (75% static locations drifting by 1%
+    # per frame): dense attention of all tokens with rotated Q/K whose channel groups are
+    # reused from the neighbouring token when their relative RMS difference is below 5%.
+    "timeripple": Config("timeripple", "reuse", 21, 30, 52, 1536, 12, 128, "bf16", static_pct=75,
+                         reuse_theta=(0.05, 0.05, 0.05)),
     # LIPAR inter-frame sweep on a 33x45x80 grid, 75% static locations, sigma = 0.6.
     "lipar": Config(
         "lipar", "lipar", 33, 45, 80, 3072, 24, 128, "bf16", static_pct=75,
