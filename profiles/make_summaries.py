@@ -167,6 +167,12 @@ EXTRA = [
      "LIPAR pass with the long/short-term mask + restoration, 33x45x80 -> N=118800, D=3072, 24 x 128",
      "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_lipar_lif -o run -- "
      "python3 bench.py --workload lipar_lif --steps 10 --warmup 1"),
+    ("prof_tr", "timeripple_reuse_kernel_trace.txt",
+     "dense pass with Timeripple partial-score reuse, 21x30x52 -> N=32760, D=1536, 12 x 128 "
+     "(bench pass with reuse + pass without reuse + the reuse kernels timed alone; the 512 MB "
+     "reduce is the bench's MALL flush)",
+     "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_tr -o run -- "
+     "python3 bench.py --workload timeripple --steps 10 --warmup 2"),
     ("prof_rc", "layer_step_wan13b_rope_causal_kernel_trace.txt",
      "pruned layer step with 3D RoPE and frame-causal attention, 21x30x52 -> N=32760, D=1536, 12 x 128",
      "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_rc -o run -- "
