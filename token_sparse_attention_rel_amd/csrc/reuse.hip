@@ -16,11 +16,11 @@
 // attention with reused partial scores.
 //
 // Three kernels, each a flat pass:
-//   delta_src: L = d/8 lanes per (token, head), 16-byte slices, shuffle sums;
+//   delta_src: L = d/8 lanes per (token, head), 16-byte slices, sums by DPP lane moves;
 //   resolve:   one thread per (token, head, group) follows the sources back to the
 //              token that computes the group itself (every step moves back along
 //              an axis, so a chain is at most frame + row + column steps long);
-//   copy:      one thread per 4-byte channel pair writes the effective row.
+//   copy:      one workgroup per token writes its effective row in 4-byte channel pairs.
 #include <math.h>
 
 #include "common.h"
@@ -41,12 +41,31 @@ __device__ __forceinline__ int channel_group(const ReuseGeom& g, int c) {
   return c < g.d_t ? 0 : (c < g.d_t + g.d_s ? 1 : 2);
 }
 
-// The token one step back along axis a (0 time, 1 height, 2 width), or -1.
-__device__ __forceinline__ long axis_back(const ReuseGeom& g, long t, int a) {
-  if (a == 0) return t >= g.hw ? t - g.hw : -1;
-  const long in_frame = t % g.hw;
-  if (a == 1) return in_frame >= g.width ? t - g.width : -1;
-  return in_frame % g.width ? t - 1 : -1;
+// The token one step back along axis a (0 time, 1 height, 2 width), or -1.  Token
+// indices fit 31 bits (the ABI checks), so the divisions are 32-bit ones.
+__device__ __forceinline__ long axis_back(const ReuseGeom& g, uint32_t t, int a) {
+  const uint32_t hw = static_cast<uint32_t>(g.hw), w = static_cast<uint32_t>(g.width);
+  if (a == 0) return t >= hw ? static_cast<long>(t - hw) : -1;
+  const uint32_t in_frame = t % hw;
+  if (a == 1) return in_frame >= w ? static_cast<long>(t - w) : -1;
+  return in_frame % w ? static_cast<long>(t) - 1 : -1;
+}
+
+// Data-parallel-primitive moves inside a row of 16 lanes (quad_perm 1,0,3,2 and
+// 2,3,0,1, half-row mirror, row mirror): summing a value with each in turn leaves
+// every lane of an aligned group of 4, 8 or 16 lanes holding the group's sum.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+template <int L>
+__device__ __forceinline__ float lane_group_sum(float v) {
+  v += dpp_move<0xB1>(v);  // quad_perm [1, 0, 3, 2]
+  v += dpp_move<0x4E>(v);  // quad_perm [2, 3, 0, 1]
+  if constexpr (L >= 8) v += dpp_move<0x141>(v);   // row_half_mirror: lane i <-> 7 - i
+  if constexpr (L >= 16) v += dpp_move<0x140>(v);  // row_mirror: lane i <-> 15 - i
+  return v;
 }
 
 template <int HD>
@@ -55,17 +74,20 @@ __global__ __launch_bounds__(256) void reuse_delta_src_kernel(const uint16_t* __
                                                               int* __restrict__ src, int* __restrict__ src_copy,
                                                               float* __restrict__ delta_out) {
   constexpr int L = HD / 8;  // lanes per (token, head), 8 channels each
-  const long pair = (static_cast<long>(blockIdx.x) * 256 + threadIdx.x) / L;
+  // (token, head) pairs fit 31 bits: n * heads * 3 < 2^31 (the ABI checks); the thread
+  // index itself may not, so the pair is formed from the block index in 64 bits
+  const uint32_t pair = static_cast<uint32_t>(static_cast<uint64_t>(blockIdx.x) * (256 / L) + threadIdx.x / L);
   const int sub = threadIdx.x % L;
-  const long n_pairs = geo.n * geo.heads;
-  const bool live = pair < n_pairs;
-  const long t = live ? pair / geo.heads : 0;
-  const int h = static_cast<int>(pair % geo.heads);
+  const uint32_t heads = static_cast<uint32_t>(geo.heads);
+  const bool live = pair < static_cast<uint32_t>(geo.n * geo.heads);
+  const uint32_t t = live ? pair / heads : 0u;
+  const int h = static_cast<int>(pair - t * heads);
   const long dim = static_cast<long>(geo.heads) * HD;
   const long col = static_cast<long>(h) * HD + 8 * sub;
+  const long tl = t;
 
   float own[8];
-  unpack8(*reinterpret_cast<const u32x4*>(v + t * dim + col), own);
+  unpack8(*reinterpret_cast<const u32x4*>(v + tl * dim + col), own);
   int grp[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) grp[e] = channel_group(geo, 8 * sub + e);
@@ -76,7 +98,7 @@ __global__ __launch_bounds__(256) void reuse_delta_src_kernel(const uint16_t* __
   for (int a = 0; a < 3; ++a) {
     nb[a] = live ? axis_back(geo, t, a) : -1;
     float w[8];
-    unpack8(*reinterpret_cast<const u32x4*>(v + (nb[a] >= 0 ? nb[a] : t) * dim + col), w);
+    unpack8(*reinterpret_cast<const u32x4*>(v + (nb[a] >= 0 ? nb[a] : tl) * dim + col), w);
     float s_num = 0.f, s_den = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -86,14 +108,10 @@ __global__ __launch_bounds__(256) void reuse_delta_src_kernel(const uint16_t* __
         s_den = fmaf(own[e], own[e], s_den);
       }
     }
-    // sum over the L lanes of this (token, head): xor butterflies inside the lane group
-#pragma unroll
-    for (int off = L / 2; off > 0; off >>= 1) {
-      s_num += __shfl_xor(s_num, off, kWave);
-      s_den += __shfl_xor(s_den, off, kWave);
-    }
-    num[a] = s_num;
-    den[a] = s_den;
+    // sum over the L lanes of this (token, head)
+    static_assert(L == 8 || L == 16, "lane groups of 8 or 16");
+    num[a] = lane_group_sum<L>(s_num);
+    den[a] = lane_group_sum<L>(s_den);
   }
   if (!live || sub != 0) return;
   const float theta[3] = {th0, th1, th2};
@@ -107,10 +125,10 @@ __global__ __launch_bounds__(256) void reuse_delta_src_kernel(const uint16_t* __
     else
       delta[a] = sqrtf(num[a]) / sqrtf(den[a]);
   }
-  const long base = pair * 3;
+  const long base = static_cast<long>(pair) * 3;
 #pragma unroll
   for (int gi = 0; gi < 3; ++gi) {
-    long from = t;
+    long from = tl;
 #pragma unroll
     for (int a = 2; a >= 0; --a)  // the first qualifying axis in time, height, width order wins
       if (a != gi && delta[a] < theta[a]) from = nb[a];
@@ -123,15 +141,18 @@ __global__ __launch_bounds__(256) void reuse_delta_src_kernel(const uint16_t* __
 // root[(t*heads + h)*3 + g] = the token whose own channels group g of token t ends up with.
 __global__ __launch_bounds__(256) void reuse_resolve_kernel(const int* __restrict__ src, long n_entries,
                                                             int heads, int* __restrict__ root) {
-  const long i = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= n_entries) return;
-  const long hg = i % (3L * heads);  // (head, group) part of the entry index
-  long s = i / (3L * heads);
-  long nx = src[i];
-  // sources strictly precede their tokens: at most s steps
-  for (long it = 0; nx != s && it <= i; ++it) {
+  // entries fit 31 bits (the ABI checks n * heads * 3 < 2^31)
+  const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+  if (i >= static_cast<uint64_t>(n_entries)) return;
+  const uint32_t per_token = 3u * static_cast<uint32_t>(heads);
+  const uint32_t s0 = i / per_token;
+  const uint32_t hg = i - s0 * per_token;  // (head, group) part of the entry index
+  uint32_t s = s0;
+  uint32_t nx = static_cast<uint32_t>(src[i]);
+  // sources strictly precede their tokens: at most s0 steps
+  for (uint32_t it = 0; nx != s && it <= s0; ++it) {
     s = nx;
-    nx = src[s * 3L * heads + hg];
+    nx = static_cast<uint32_t>(src[s * per_token + hg]);
   }
   root[i] = static_cast<int>(s);
 }
@@ -141,15 +162,15 @@ template <int HD>
 __global__ __launch_bounds__(256) void reuse_copy_kernel(const uint32_t* __restrict__ v, const int* __restrict__ root,
                                                          ReuseGeom geo, uint32_t* __restrict__ eff) {
   constexpr int WPH = HD / 2;  // 4-byte channel pairs per head
-  const long i = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
-  const long words = static_cast<long>(geo.heads) * WPH;
-  if (i >= geo.n * words) return;
-  const long t = i / words;
-  const long w = i - t * words;
-  const int h = static_cast<int>(w / WPH);
-  const int g = channel_group(geo, static_cast<int>(2 * (w % WPH)));  // group bounds are even
-  const long from = root[(t * geo.heads + h) * 3 + g];
-  eff[i] = v[from * words + w];
+  const long t = blockIdx.x;  // one workgroup per token
+  const int words = geo.heads * WPH;
+  const int* rt = root + t * geo.heads * 3;
+  uint32_t* out = eff + t * words;
+  for (int w = threadIdx.x; w < words; w += 256) {
+    const int h = w / WPH;
+    const int g = channel_group(geo, 2 * (w % WPH));  // group bounds are even
+    out[w] = v[static_cast<long>(rt[h * 3 + g]) * words + w];
+  }
 }
 
 hipError_t launch_reuse(const uint16_t* v, long n, int heads, int head_dim, long height, long width,
@@ -175,12 +196,11 @@ hipError_t launch_reuse(const uint16_t* v, long n, int heads, int head_dim, long
   const long entries = pairs * 3;
   hipLaunchKernelGGL(reuse_resolve_kernel, dim3(static_cast<unsigned>((entries + 255) / 256)), dim3(256), 0, s,
                      ws_src, entries, heads, ws_root);
-  const long words = n * heads * (head_dim / 2);
   if (head_dim == 128)
-    hipLaunchKernelGGL(reuse_copy_kernel<128>, dim3(static_cast<unsigned>((words + 255) / 256)), dim3(256), 0, s,
+    hipLaunchKernelGGL(reuse_copy_kernel<128>, dim3(static_cast<unsigned>(n)), dim3(256), 0, s,
                        reinterpret_cast<const uint32_t*>(v), ws_root, geo, reinterpret_cast<uint32_t*>(eff));
   else
-    hipLaunchKernelGGL(reuse_copy_kernel<64>, dim3(static_cast<unsigned>((words + 255) / 256)), dim3(256), 0, s,
+    hipLaunchKernelGGL(reuse_copy_kernel<64>, dim3(static_cast<unsigned>(n)), dim3(256), 0, s,
                        reinterpret_cast<const uint32_t*>(v), ws_root, geo, reinterpret_cast<uint32_t*>(eff));
   return hipGetLastError();
 }
