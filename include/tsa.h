@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define TSA_ABI_VERSION 5
+#define TSA_ABI_VERSION 6
 
 typedef uint16_t tsa_bf16;
 
@@ -195,6 +195,27 @@ tsa_status tsa_qkv_active_rope(const void* x, int x_dtype, int64_t n_x_rows, con
                                tsa_bf16* k_out, tsa_bf16* v_out, int out_is_cache, int64_t n_cache,
                                const tsa_bf16* eps, int64_t src_row_offset, float sigma, int heads,
                                int64_t height, int64_t width, float rope_base, void* stream);
+
+/*
+ * a4-a6 for rows prepared beforehand: [LIPAR] §2.C recovered rows gathered once
+ * into a compact buffer (tsa_gather_rows) and projected here, so the recovery
+ * arithmetic runs once per row instead of once per output-feature tile.
+ * Row r of the product reads a[r] and belongs to token t = rows[r]:
+ *   K/V[r] = bf16(a[r] @ W_k/v^T) written to cache row t; Q[r] likewise to
+ * q_out[r] (compact) when q_out is not NULL.  heads > 0: Q and K rotated by the
+ * 3D position of token t as in tsa_qkv_active_rope ([Timeripple] Metodología §1).
+ *   a          device bf16 [n, dim].
+ *   rows       device i32[n], each < n_cache.
+ *   w_qkv      as in tsa_qkv_active.
+ *   k_cache, v_cache  device bf16 [n_cache, dim].
+ *   heads, height, width, rope_base  rotary positions (heads = 0: none).
+ * dim a multiple of 64; n*dim*2 and 3*dim*dim*2 below 2^31 bytes.
+ * Errors: INVALID_ARG, SHAPE, ALIGNMENT, HIP.
+ */
+tsa_status tsa_qkv_rows_to_cache(const tsa_bf16* a, int64_t n, int64_t dim, const int32_t* rows,
+                                 const tsa_bf16* w_qkv, tsa_bf16* q_out, tsa_bf16* k_cache, tsa_bf16* v_cache,
+                                 int64_t n_cache, int heads, int64_t height, int64_t width, float rope_base,
+                                 void* stream);
 
 /*
  * a6: [HSA] §2.2 item 2 -- the fresh K/V of the active tokens overwrite

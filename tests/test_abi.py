@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(root):
 
 
 def test_version_and_status_strings():
-    assert tsa.abi_version() == 5
+    assert tsa.abi_version() == 6
     assert tsa.status_string(0) == "ok"
     assert "shape" in tsa.status_string(B.ERR_SHAPE)
     assert tsa.status_string(99) == "unknown status"
@@ -234,3 +234,22 @@ def test_reuse_validation():
     assert ru(src=A + 2) == B.ERR_ALIGNMENT
     assert ru(ws=None) == B.ERR_WORKSPACE
     assert ru(wsb=100) == B.ERR_WORKSPACE
+
+
+def test_qkv_rows_to_cache_validation():
+    f = lib()
+
+    def rc(**kw):
+        a = dict(a=A, n=16, dim=128, rows=A, w=A, q=None, k=A, v=A, nc=64, heads=0, h=1, w_=1, base=10000.0)
+        a.update(kw)
+        return f.tsa_qkv_rows_to_cache(a["a"], a["n"], a["dim"], a["rows"], a["w"], a["q"], a["k"], a["v"],
+                                       a["nc"], a["heads"], a["h"], a["w_"], a["base"], None)
+    assert rc(n=0) == B.OK
+    assert rc(rows=None) == B.ERR_INVALID_ARG
+    assert rc(a=None) == B.ERR_INVALID_ARG
+    assert rc(dim=96) == B.ERR_SHAPE
+    assert rc(heads=3) == B.ERR_SHAPE
+    assert rc(heads=2, h=0) == B.ERR_SHAPE
+    assert rc(heads=2, h=4, w_=4, base=0.0) == B.ERR_INVALID_ARG
+    assert rc(a=U) == B.ERR_ALIGNMENT
+    assert rc(rows=A + 2) == B.ERR_ALIGNMENT

@@ -385,6 +385,39 @@ def test_qkv_large_tile_sampled(src):
     assert not kc[others].any() and not vc[others].any()
 
 
+@pytest.mark.parametrize("n_x,m,dim,rope", [(2000, 777, 1536, None), (9000, 7461, 3072, None),
+                                            (1200, 500, 512, (6, 10, 4))])
+def test_rows_to_cache_equals_fused_recovery(n_x, m, dim, rope):
+    """Recovered rows gathered once and projected into their cache rows equal the fused
+    recovery projection bit for bit (the same blend, the same GEMM arithmetic)."""
+    t = tsa()
+    g = torch.Generator().manual_seed(m)
+    x = _randn_bf16(g, n_x, dim)
+    eps = _randn_bf16(g, n_x, dim)
+    w = (torch.randn(3 * dim, dim, generator=g) / math.sqrt(dim)).to(torch.bfloat16)
+    rows = G.dev(torch.from_numpy(np.sort(np.random.default_rng(m).choice(n_x, m, replace=False)).astype(np.int32)))
+    off, sigma = n_x // 7, 0.6
+    caches = [torch.zeros(n_x, dim, dtype=torch.bfloat16, device="cuda") for _ in range(4)]
+    xd, ed, wd = G.dev(x), G.dev(eps), G.dev(w)
+    if rope is None:
+        t.qkv_active(xd, rows, m, wd, k_out=caches[0], v_out=caches[1], out_is_cache=True, n_cache=n_x, eps=ed,
+                     src_row_offset=off, sigma=sigma)
+    else:
+        h, wd_, heads = rope
+        t.qkv_active_rope(xd, rows, m, wd, heads, h, wd_, k_out=caches[0], v_out=caches[1], out_is_cache=True,
+                          n_cache=n_x, eps=ed, src_row_offset=off, sigma=sigma)
+    rec = torch.empty(m, dim, dtype=torch.bfloat16, device="cuda")
+    t.gather_rows(xd, rows, m, rec, eps=ed, src_row_offset=off, sigma=sigma)
+    if rope is None:
+        t.qkv_rows_to_cache(rec, rows, m, wd, caches[2], caches[3])
+    else:
+        t.qkv_rows_to_cache(rec, rows, m, wd, caches[2], caches[3], rope=(h, wd_, 10000.0), heads=heads)
+    torch.cuda.synchronize()
+    assert torch.equal(caches[0], caches[2]) and torch.equal(caches[1], caches[3])
+    others = torch.from_numpy(np.setdiff1d(np.arange(n_x), rows.cpu().numpy())).cuda()
+    assert not caches[2][others].any() and caches[2][rows.long()].any()
+
+
 # --------------------------------------------------------------- attention
 
 @pytest.mark.parametrize("n_q,n_kv,heads,hd", [(1, 1, 1, 64), (37, 53, 3, 64), (128, 64, 2, 128),

@@ -29,6 +29,7 @@ from ._binding import (
     lib_path,
     qkv_active,
     qkv_active_rope,
+    qkv_rows_to_cache,
     restore_frames,
     reuse_workspace_bytes,
     scatter_out,

@@ -53,6 +53,7 @@ _SIGNATURES = {
     "tsa_lif_mask": (_int, [_vp, _int, _i64, _i64, _i64, _int, _f32, _f32, _vp, _vp, _vp, _vp]),
     "tsa_restore_frames": (_int, [_vp, _int, _vp, _i64, _i64, _i64, _vp]),
     "tsa_reuse_workspace_bytes": (_size, [_i64, _int]),
+    "tsa_qkv_rows_to_cache": (_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _int, _i64, _i64, _f32, _vp]),
     "tsa_timeripple_reuse": (_int, [_vp, _i64, _int, _int, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _size, _vp]),
 }
 
@@ -244,6 +245,17 @@ def restore_frames(buf, mask, frames, hw, stream=None):
     st = lib().tsa_restore_frames(_ptr(buf), _dtype_code(buf), _ptr(mask), int(frames), int(hw),
                                   int(buf.shape[1]), _stream(stream))
     _check("tsa_restore_frames", st)
+
+
+def qkv_rows_to_cache(a, rows, n, w_qkv, k_cache, v_cache, *, q_out=None, rope=None, heads=0, stream=None):
+    """K/V (and Q) of compact rows a[r], written to cache rows rows[r] (tsa_qkv_rows_to_cache);
+    rope = (height, width, base) with heads > 0 rotates Q and K by the tokens' positions."""
+    h, w, base = rope if rope is not None else (1, 1, 10000.0)
+    st = lib().tsa_qkv_rows_to_cache(_ptr(a), int(n), int(a.shape[1]), _ptr(rows), _ptr(w_qkv), _ptr(q_out),
+                                      _ptr(k_cache), _ptr(v_cache), int(k_cache.shape[0]),
+                                      int(heads) if rope is not None else 0, int(h), int(w), float(base),
+                                      _stream(stream))
+    _check("tsa_qkv_rows_to_cache", st)
 
 
 def reuse_workspace_bytes(n_rows, heads):

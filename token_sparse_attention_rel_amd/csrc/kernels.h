@@ -44,6 +44,8 @@ struct QkvOut {
   uint16_t* k;      // compact [n, dim] or cache [n_cache, dim]
   uint16_t* v;
   int to_cache;     // k/v row r goes to row rows[r]
+  const int* rows = nullptr;  // token of product row r when it differs from the row read
+                              // (compact input rows); nullptr: the token read
 };
 // 3D rotary positions applied to Q and K in the epilogue (heads == 0: none).
 struct RopeSpec {

@@ -60,7 +60,8 @@ enum { kSrcBf16 = 0, kSrcF32 = 1, kSrcRecover = 2 };
 struct GemmArgs {
   const void* x;
   long n_x_rows;
-  const int* rows;
+  const int* rows;      // token row read for product row r (nullptr: r)
+  const int* out_rows;  // token of product row r for the cache rows and positions
   const uint16_t* eps;
   long src_off;
   float sigma;
@@ -273,7 +274,7 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void qkv_gemm_kernel(
   for (int j = 0; j < kWaveBT; ++j) {
     const long r = t_base + (wt * kWaveBT + j) * 32 + l32;
     if (r >= a.n) continue;
-    const long t = a.rows ? static_cast<long>(a.rows[r]) : r;
+    const long t = a.out_rows ? static_cast<long>(a.out_rows[r]) : r;
     float pos[3] = {0.f, 0.f, 0.f};
     if (a.rope_d) {
       const unsigned tu = static_cast<unsigned>(t), hw = static_cast<unsigned>(a.rope_hw),
@@ -331,6 +332,7 @@ hipError_t launch_qkv(const RowSource& src, long n, long dim, const uint16_t* w_
   a.x = src.x;
   a.n_x_rows = src.n_x_rows;
   a.rows = src.rows;
+  a.out_rows = out.rows ? out.rows : src.rows;
   a.eps = src.eps;
   a.src_off = src.src_off;
   a.sigma = src.sigma;

@@ -196,6 +196,35 @@ tsa_status tsa_qkv_active_rope(const void* x, int x_dtype, int64_t n_x_rows, con
   return from_hip(tsa::launch_qkv(src, n, dim, w_qkv, out, rope, as_stream(stream)));
 }
 
+tsa_status tsa_qkv_rows_to_cache(const tsa_bf16* a, int64_t n, int64_t dim, const int32_t* rows,
+                                 const tsa_bf16* w_qkv, tsa_bf16* q_out, tsa_bf16* k_cache, tsa_bf16* v_cache,
+                                 int64_t n_cache, int heads, int64_t height, int64_t width, float rope_base,
+                                 void* stream) {
+  if (!a || !rows || !w_qkv || !k_cache || !v_cache) return TSA_ERR_INVALID_ARG;
+  if (n < 0 || n > kMaxRows || n_cache < 0 || n_cache > kMaxRows) return TSA_ERR_SHAPE;
+  if (dim <= 0 || dim % 64 != 0 || dim > (int64_t{1} << 20)) return TSA_ERR_SHAPE;
+  if (n * dim * 2 > kMaxBufferBytes || 3 * dim * dim * 2 > kMaxBufferBytes) return TSA_ERR_SHAPE;
+  tsa::RopeSpec rope;
+  if (heads != 0) {
+    if (heads < 1 || heads > 4096 || dim % heads != 0 || (dim / heads) % 2 != 0 || dim / heads < 6)
+      return TSA_ERR_SHAPE;
+    if (height < 1 || width < 1 || height > kMaxRows || width > kMaxRows || height * width > kMaxRows)
+      return TSA_ERR_SHAPE;
+    if (!(rope_base > 0.f) || isinf(rope_base)) return TSA_ERR_INVALID_ARG;
+    rope.heads = heads;
+    rope.height = height;
+    rope.width = width;
+    rope.log2_base = log2f(rope_base);
+  }
+  if (!aligned16(a) || !aligned16(w_qkv) || (q_out && !aligned16(q_out)) || !aligned16(k_cache) ||
+      !aligned16(v_cache) || !aligned4(rows))
+    return TSA_ERR_ALIGNMENT;
+  if (n == 0) return TSA_OK;
+  RowSource src{a, TSA_BF16, n, nullptr, nullptr, 0, 0.f};
+  tsa::QkvOut out{q_out, k_cache, v_cache, 1, rows};
+  return from_hip(tsa::launch_qkv(src, n, dim, w_qkv, out, rope, as_stream(stream)));
+}
+
 tsa_status tsa_kv_cache_sync(const tsa_bf16* k_a, const tsa_bf16* v_a, const int32_t* rows,
                              int64_t n, tsa_bf16* k_cache, tsa_bf16* v_cache, int64_t n_cache,
                              int64_t dim, void* stream) {

@@ -178,9 +178,12 @@ class PrunedAttentionLayer:
                   out_is_cache=True, n_cache=self.n, stream=stream)
         n_p = self.n - k
         if n_p:
-            self._qkv(x, self.pidx, n_p, q_out=None, k_out=self.k_cache, v_out=self.v_cache,
-                      out_is_cache=True, n_cache=self.n, eps=eps, src_row_offset=hw, sigma=sigma,
-                      stream=stream)
+            # recovered rows built once (gather), then projected into their cache rows: the
+            # blend then runs once per row instead of once per output-feature tile
+            rec = self._compact_bufs()[0]
+            B.gather_rows(x, self.pidx, n_p, rec, eps=eps, src_row_offset=hw, sigma=sigma, stream=stream)
+            B.qkv_rows_to_cache(rec, self.pidx, n_p, self.w_qkv, self.k_cache, self.v_cache, rope=self.rope,
+                                heads=self.heads, stream=stream)
         if k:
             self._attend(k, self.out, self.idx, rows=self.idx, stream=stream)
 
