@@ -124,7 +124,7 @@ def test_topk_select_and_compact_bit_exact_with_ties(n):
         assert np.array_equal(pidx.cpu().numpy()[:n - k], wp)
 
 
-@pytest.mark.parametrize("n,k", [(32760, 9828), (100001, 30000), (118800, 45619), (65536, 1)])
+@pytest.mark.parametrize("n,k", [(32760, 9828), (100001, 30000), (118800, 45619), (65536, 1), (1000003, 333333)])
 def test_topk_distinct_scores_multi_chunk(n, k):
     """Continuous scores (no ties): the selected set is the top k of the kernel's own fp32
     scores, decided by the oracle on those same values."""
