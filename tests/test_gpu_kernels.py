@@ -32,7 +32,8 @@ def _randn_bf16(gen, *shape, scale=1.0):
 # ------------------------------------------------------------------ scores
 
 @pytest.mark.parametrize("dtype,n,dim", [(torch.float32, 256, 128), (torch.bfloat16, 1000, 1536),
-                                         (torch.bfloat16, 77, 5120)])
+                                         (torch.bfloat16, 77, 5120), (torch.float32, 300, 768),
+                                         (torch.bfloat16, 130, 512)])
 def test_scores_match_oracle(dtype, n, dim):
     t = tsa()
     g = torch.Generator().manual_seed(n + dim)
@@ -209,10 +210,13 @@ def test_assign_groups_bit_exact():
 
 # -------------------------------------------------------------- row movers
 
-def test_gather_cache_sync_scatter_bit_exact():
+@pytest.mark.parametrize("n,dim,na_", [(3000, 1536, 901), (700, 512, 333), (400, 3072, 97), (300, 5120, 77),
+                                       (64, 1536, 1)])
+def test_gather_cache_sync_scatter_bit_exact(n, dim, na_):
+    """Row widths for each loader shape (2 or 4 slices per lane with two rows per wave, 8 with
+    one, rows longer than one pass) and odd row counts (a wave with one live row)."""
     t = tsa()
     g = torch.Generator().manual_seed(11)
-    n, dim, na_ = 3000, 1536, 901
     x = _randn_bf16(g, n, dim)
     rows = torch.from_numpy(np.sort(np.random.default_rng(1).choice(n, na_, replace=False)).astype(np.int32))
     xd, rd = G.dev(x), G.dev(rows)
@@ -221,7 +225,7 @@ def test_gather_cache_sync_scatter_bit_exact():
     assert torch.equal(dst.cpu(), x[rows.long()])
     # recovery rows: (1 - sigma) x[t - off] + sigma eps[t], first rows have no previous row
     eps = _randn_bf16(g, n, dim)
-    off = 500
+    off = min(500, n // 3)
     for sigma in (0.0, 1.0, 0.6):
         t.gather_rows(xd, rd, na_, dst, eps=G.dev(eps), src_row_offset=off, sigma=sigma)
         want = ref.recover_rows(G.host64(x), G.host64(eps), rows.numpy(), off, sigma)

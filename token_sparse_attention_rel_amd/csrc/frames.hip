@@ -135,7 +135,8 @@ __global__ __launch_bounds__(kLifThreads) void lif_mask_kernel(const T* __restri
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
       const long sl = threadIdx.x + static_cast<long>(kLifThreads) * j;
-      dst[j] = sl < n_sl ? *reinterpret_cast<const u32x4*>(row + sl * V) : u32x4{0u, 0u, 0u, 0u};
+      dst[j] = sl < n_sl ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + sl * V))
+                         : u32x4{0u, 0u, 0u, 0u};
     }
   };
   auto unpack_row = [&](const u32x4 (&r)[CPT], float (*dst)[V]) {
@@ -257,7 +258,7 @@ __global__ __launch_bounds__(256) void restore_kernel(u32x4* __restrict__ buf, c
     for (int i = 0; i < kF; ++i) {
       const long f = f0 + i;
       kept[i] = f < frames && mask[f * hw + loc];
-      if (kept[i]) r[i] = buf[(f * hw + loc) * slices + sl];
+      if (kept[i]) r[i] = __builtin_nontemporal_load(buf + (f * hw + loc) * slices + sl);
     }
 #pragma unroll
     for (int i = 0; i < kF; ++i) {

@@ -43,7 +43,9 @@ struct RowLoad<float> {  // fp32: 4 elements per 16-byte load
 // One wave per token row: each lane accumulates sum|x - r| and sum|r| over
 // its 16-byte slices, then a butterfly reduction.  The slices of a lane are
 // loaded in batches of B, all loads of a batch issued before any is used, so a
-// wave keeps 2*B 16-byte loads in flight.  Fixed order: deterministic.
+// wave keeps 2*B 16-byte loads in flight.  Nontemporal loads: each row is read
+// once (33 against 36 us for 2 x 32760 rows of 1536 bf16 with a flushed MALL).
+// Fixed order: deterministic.
 template <typename T, int B>
 __global__ __launch_bounds__(256) void score_kernel(const T* __restrict__ x_cur,
                                                     const T* __restrict__ ref,
@@ -67,8 +69,8 @@ __global__ __launch_bounds__(256) void score_kernel(const T* __restrict__ x_cur,
 #pragma unroll
     for (int j = 0; j < B; ++j) {
       const long c = c0 + lane + 64 * j;
-      ra[j] = c < nsl ? a[c] : u32x4{0u, 0u, 0u, 0u};
-      rb[j] = c < nsl ? b[c] : u32x4{0u, 0u, 0u, 0u};
+      ra[j] = c < nsl ? __builtin_nontemporal_load(a + c) : u32x4{0u, 0u, 0u, 0u};
+      rb[j] = c < nsl ? __builtin_nontemporal_load(b + c) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int j = 0; j < B; ++j) {
@@ -505,11 +507,15 @@ hipError_t launch_scores(const void* x_cur, const void* x_ref, long ref_off, lon
   if (dtype == kDtypeBf16) {
     if (per_lane <= 2)
       launch_scores_t<uint16_t, 2>(x_cur, x_ref, ref_off, n_rows, dim, relative, scores, s);
+    else if (per_lane == 3)
+      launch_scores_t<uint16_t, 3>(x_cur, x_ref, ref_off, n_rows, dim, relative, scores, s);
     else
       launch_scores_t<uint16_t, 4>(x_cur, x_ref, ref_off, n_rows, dim, relative, scores, s);
   } else {
     if (per_lane <= 2)
       launch_scores_t<float, 2>(x_cur, x_ref, ref_off, n_rows, dim, relative, scores, s);
+    else if (per_lane == 3)
+      launch_scores_t<float, 3>(x_cur, x_ref, ref_off, n_rows, dim, relative, scores, s);
     else
       launch_scores_t<float, 4>(x_cur, x_ref, ref_off, n_rows, dim, relative, scores, s);
   }
