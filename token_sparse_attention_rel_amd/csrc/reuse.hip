@@ -20,7 +20,7 @@
 //   resolve:   one thread per (token, head, group) follows the sources back to the
 //              token that computes the group itself (every step moves back along
 //              an axis, so a chain is at most frame + row + column steps long);
-//   copy:      one workgroup per token writes its effective row in 4-byte channel pairs.
+//   copy:      one wave per token writes its effective row in 16-byte chunks.
 #include <math.h>
 
 #include "common.h"
@@ -41,14 +41,14 @@ __device__ __forceinline__ int channel_group(const ReuseGeom& g, int c) {
   return c < g.d_t ? 0 : (c < g.d_t + g.d_s ? 1 : 2);
 }
 
-// The token one step back along axis a (0 time, 1 height, 2 width), or -1.  Token
-// indices fit 31 bits (the ABI checks), so the divisions are 32-bit ones.
-__device__ __forceinline__ long axis_back(const ReuseGeom& g, uint32_t t, int a) {
+// The tokens one step back along each axis (time, height, width), -1 where there is
+// none.  Token indices fit 31 bits (the ABI checks), so the divisions are 32-bit ones.
+__device__ __forceinline__ void axis_back3(const ReuseGeom& g, uint32_t t, long nb[3]) {
   const uint32_t hw = static_cast<uint32_t>(g.hw), w = static_cast<uint32_t>(g.width);
-  if (a == 0) return t >= hw ? static_cast<long>(t - hw) : -1;
   const uint32_t in_frame = t % hw;
-  if (a == 1) return in_frame >= w ? static_cast<long>(t - w) : -1;
-  return in_frame % w ? static_cast<long>(t) - 1 : -1;
+  nb[0] = t >= hw ? static_cast<long>(t - hw) : -1;
+  nb[1] = in_frame >= w ? static_cast<long>(t - w) : -1;
+  nb[2] = in_frame % w ? static_cast<long>(t) - 1 : -1;
 }
 
 // Data-parallel-primitive moves inside a row of 16 lanes (quad_perm 1,0,3,2 and
@@ -81,24 +81,30 @@ __global__ __launch_bounds__(256) void reuse_delta_src_kernel(const uint16_t* __
   const uint32_t heads = static_cast<uint32_t>(geo.heads);
   const bool live = pair < static_cast<uint32_t>(geo.n * geo.heads);
   const uint32_t t = live ? pair / heads : 0u;
-  const int h = static_cast<int>(pair - t * heads);
+  const int h = live ? static_cast<int>(pair - t * heads) : 0;  // dead lanes read row 0, head 0
   const long dim = static_cast<long>(geo.heads) * HD;
   const long col = static_cast<long>(h) * HD + 8 * sub;
   const long tl = t;
 
+  long nb[3];
+  axis_back3(geo, t, nb);
+  if (!live) nb[0] = nb[1] = nb[2] = -1;
+  // all four rows in flight before any is used
+  u32x4 raw[4];
+  raw[0] = *reinterpret_cast<const u32x4*>(v + tl * dim + col);
+#pragma unroll
+  for (int a = 0; a < 3; ++a) raw[1 + a] = *reinterpret_cast<const u32x4*>(v + (nb[a] >= 0 ? nb[a] : tl) * dim + col);
   float own[8];
-  unpack8(*reinterpret_cast<const u32x4*>(v + tl * dim + col), own);
+  unpack8(raw[0], own);
   int grp[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) grp[e] = channel_group(geo, 8 * sub + e);
 
   float num[3], den[3];
-  long nb[3];
 #pragma unroll
   for (int a = 0; a < 3; ++a) {
-    nb[a] = live ? axis_back(geo, t, a) : -1;
     float w[8];
-    unpack8(*reinterpret_cast<const u32x4*>(v + (nb[a] >= 0 ? nb[a] : tl) * dim + col), w);
+    unpack8(raw[1 + a], w);
     float s_num = 0.f, s_den = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -157,19 +163,35 @@ __global__ __launch_bounds__(256) void reuse_resolve_kernel(const int* __restric
   root[i] = static_cast<int>(s);
 }
 
-// eff[t, h*HD + 2w .. +1] = v[root(t, h, group(2w)), same channels]
+// eff[t, chunk c] = the 8 channels of chunk c, each taken from the resolved token of
+// its group.  One wave per token, 16-byte chunks; a chunk crosses at most one group
+// bound (groups are at least 20 channels wide), and bounds are even, so a chunk
+// that straddles one is blended from two rows in 4-byte channel pairs.
 template <int HD>
-__global__ __launch_bounds__(256) void reuse_copy_kernel(const uint32_t* __restrict__ v, const int* __restrict__ root,
-                                                         ReuseGeom geo, uint32_t* __restrict__ eff) {
-  constexpr int WPH = HD / 2;  // 4-byte channel pairs per head
-  const long t = blockIdx.x;  // one workgroup per token
-  const int words = geo.heads * WPH;
+__global__ __launch_bounds__(256) void reuse_copy_kernel(const u32x4* __restrict__ v, const int* __restrict__ root,
+                                                         ReuseGeom geo, u32x4* __restrict__ eff) {
+  constexpr int CPH = HD / 8;  // chunks per head
+  const long t = static_cast<long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= geo.n) return;
+  const int lane = threadIdx.x & 63;
+  const int chunks = geo.heads * CPH;
   const int* rt = root + t * geo.heads * 3;
-  uint32_t* out = eff + t * words;
-  for (int w = threadIdx.x; w < words; w += 256) {
-    const int h = w / WPH;
-    const int g = channel_group(geo, 2 * (w % WPH));  // group bounds are even
-    out[w] = v[static_cast<long>(rt[h * 3 + g]) * words + w];
+  for (int c = lane; c < chunks; c += 64) {
+    const int h = c / CPH;
+    const int c0 = 8 * (c - h * CPH);  // first channel of the chunk within its head
+    const int g0 = channel_group(geo, c0), g1 = channel_group(geo, c0 + 7);
+    const long r0 = rt[h * 3 + g0];
+    u32x4 val = v[r0 * chunks + c];
+    if (g1 != g0) {
+      const long r1 = rt[h * 3 + g1];
+      if (r1 != r0) {
+        const u32x4 w = v[r1 * chunks + c];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (channel_group(geo, c0 + 2 * i) == g1) val[i] = w[i];
+      }
+    }
+    eff[t * chunks + c] = val;
   }
 }
 
@@ -196,12 +218,13 @@ hipError_t launch_reuse(const uint16_t* v, long n, int heads, int head_dim, long
   const long entries = pairs * 3;
   hipLaunchKernelGGL(reuse_resolve_kernel, dim3(static_cast<unsigned>((entries + 255) / 256)), dim3(256), 0, s,
                      ws_src, entries, heads, ws_root);
+  const dim3 copy_grid(static_cast<unsigned>((n + 3) / 4));
   if (head_dim == 128)
-    hipLaunchKernelGGL(reuse_copy_kernel<128>, dim3(static_cast<unsigned>(n)), dim3(256), 0, s,
-                       reinterpret_cast<const uint32_t*>(v), ws_root, geo, reinterpret_cast<uint32_t*>(eff));
+    hipLaunchKernelGGL(reuse_copy_kernel<128>, copy_grid, dim3(256), 0, s, reinterpret_cast<const u32x4*>(v), ws_root,
+                       geo, reinterpret_cast<u32x4*>(eff));
   else
-    hipLaunchKernelGGL(reuse_copy_kernel<64>, dim3(static_cast<unsigned>(n)), dim3(256), 0, s,
-                       reinterpret_cast<const uint32_t*>(v), ws_root, geo, reinterpret_cast<uint32_t*>(eff));
+    hipLaunchKernelGGL(reuse_copy_kernel<64>, copy_grid, dim3(256), 0, s, reinterpret_cast<const u32x4*>(v), ws_root,
+                       geo, reinterpret_cast<u32x4*>(eff));
   return hipGetLastError();
 }
 
