@@ -8,9 +8,9 @@
 // Flash-style single pass with an online softmax, bf16 MFMA, fp32 state.
 // A workgroup of 8 waves (4 for head_dim 64) owns 32 queries per wave of one
 // head.
-// Key/value tiles of 64 rows are staged row-major through two LDS buffers
-// (one barrier per tile); the next tile's global loads are in flight while
-// the current one is computed.
+// Key/value tiles of 32 rows are staged row-major through rings of four LDS
+// slots, two tiles per barrier; the next pair's global loads are in flight
+// while the current pair is computed.
 //
 // Layout trick: the score tile is computed transposed, S^T = K Q^T, with
 // v_mfma_f32_32x32x16_bf16.  In that instruction's accumulator layout a lane
@@ -109,8 +109,8 @@ constexpr long attn_piece_floats() { return attn_blocks<HD>() * 64L * (HD / 32 *
 
 // Keys [t0*BN, t1*BN) of query tile `tile` (head-major numbering).  part == nullptr:
 // normalise and write the bf16 output rows (+ LSE); otherwise write the partial
-// (unnormalised O, shift, sum) to `part` for a later merge.  ks / vs are the two
-// LDS buffers of K and V tiles.
+// (unnormalised O, shift, sum) to `part` for a later merge.  ks / vs are the
+// four-slot LDS rings of K and V tiles (tile t in slot (t - t0) mod 4).
 template <int HD, bool CAUSAL = false>
 __device__ __forceinline__ void attend_segment(const AttnArgs& a, uint16_t* ks_base, uint16_t* vs_base,
                                                long tile, long t0, long t1, float* part) {
@@ -130,7 +130,7 @@ __device__ __forceinline__ void attend_segment(const AttnArgs& a, uint16_t* ks_b
   constexpr int NCH = BN * CPR / NT;   // chunks per thread per tile (K and V each)
   static_assert(NCH >= 1, "tile too small for the workgroup");
 
-  // Buffer i of each pair; plain offsets from the LDS base keep every access an LDS one.
+  // Slot i of each ring; plain offsets from the LDS base keep every access an LDS one.
   auto ks = [&](int i) { return ks_base + i * (BN * LDK); };
   auto vs = [&](int i) { return vs_base + i * (BN * LDV); };
 
@@ -285,30 +285,38 @@ __device__ __forceinline__ void attend_segment(const AttnArgs& a, uint16_t* ks_b
   }
   const float c = a.scale_log2;
 
-  // Prologue: K tiles t0 and t0+1 in LDS, S of tile t0; registers hold K(t0+2), V(t0).
-  u32x4 kr[NCH], vr[NCH];
-  gload(kr, krs, t0 * BN);
-  sstore(ks(0), k_lds, kr);
-  gload(kr, krs, (t0 + 1) * BN);
-  sstore(ks(1), k_lds, kr);
+  // Prologue: K(t0..t0+2) and V(t0) in LDS, S of tile t0; registers hold the first
+  // pair's staging tiles K(t0+3), K(t0+4), V(t0+1), V(t0+2).
+  u32x4 kr[2][NCH], vr[2][NCH];
+  gload(kr[0], krs, t0 * BN);
+  gload(kr[1], krs, (t0 + 1) * BN);
+  gload(vr[0], vrs, t0 * BN);
+  sstore(ks(0), k_lds, kr[0]);
+  sstore(ks(1), k_lds, kr[1]);
+  sstore(vs(0), v_lds, vr[0]);
+  gload(kr[0], krs, (t0 + 2) * BN);
+  sstore(ks(2), k_lds, kr[0]);
   __syncthreads();
-  gload(kr, krs, (t0 + 2) * BN);
-  gload(vr, vrs, t0 * BN);
+  gload(kr[0], krs, (t0 + 3) * BN);
+  gload(kr[1], krs, (t0 + 4) * BN);
+  gload(vr[0], vrs, (t0 + 1) * BN);
+  gload(vr[1], vrs, (t0 + 2) * BN);
   f32x16 s_cur[QB];
   qk(ks(0), s_cur);
   mask_tail(s_cur, t0 * BN);
-  __syncthreads();  // every wave is done with K(t0) before K(t0+2) overwrites it
+  __syncthreads();  // every wave is done with K(t0) before K(t0+4) overwrites it
 
   bf16x8 p_prev[QB][2];
   // Iteration t: the softmax of tile t on the VALU, interleaved with the MFMA work
-  // PV(t-1) and QK(t+1); then stage V(t) and K(t+2) and fetch V(t+1) and K(t+3).
-  // A buffer is rewritten only after the barrier that follows its last read.
+  // PV(t-1) and QK(t+1).  Staging and the barrier come once per pair of iterations
+  // (pair_end below); a slot is rewritten only after the barrier that follows its
+  // last read.
   auto iteration = [&](long t, auto has_prev, auto has_next, auto may_mask) {
-    const int b = static_cast<int>((t - t0) & 1);
+    const int r4 = static_cast<int>((t - t0) & 3);
     // LDS reads of this iteration's MFMA operands go out first, so that their
-    // latency (and that of the barrier just passed) is covered by the softmax.
-    const uint16_t* kt = ks(b ^ 1);
-    const uint16_t* vt = vs(b ^ 1);
+    // latency is covered by the softmax.
+    const uint16_t* kt = ks((r4 + 1) & 3);  // K(t+1)
+    const uint16_t* vt = vs((r4 + 3) & 3);  // V(t-1)
     bf16x8 kf[NM];
     bf16x8 vf[2][NDB];
     if constexpr (decltype(has_next)::value) {
@@ -378,11 +386,6 @@ __device__ __forceinline__ void attend_segment(const AttnArgs& a, uint16_t* ks_b
       mask_tail(s_next, (t + 1) * BN);
     }
 
-    sstore(vs(b), v_lds, vr);
-    sstore(ks(b), k_lds, kr);
-    __syncthreads();
-    gload(vr, vrs, (t + 1) * BN);
-    gload(kr, krs, (t + 3) * BN);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       if constexpr (decltype(has_next)::value) s_cur[qb] = s_next[qb];
@@ -399,16 +402,52 @@ __device__ __forceinline__ void attend_segment(const AttnArgs& a, uint16_t* ks_b
     }
   };
 
-  if (t1 - t0 == 1) {
+  // After the second iteration of each pair (t, t+1): stage K(t+3), K(t+4), V(t+1),
+  // V(t+2) into the slots last read in the previous pair, one barrier, then fetch the
+  // next pair's staging tiles (two iterations of latency to cover).  The next pair
+  // reads K(t+3), K(t+4), V(t+1), V(t+2): published by this barrier.
+  auto pair_end = [&](long t) {
+    const int r4 = static_cast<int>((t - t0) & 3);
+    sstore(ks((r4 + 3) & 3), k_lds, kr[0]);
+    sstore(ks(r4), k_lds, kr[1]);
+    sstore(vs((r4 + 1) & 3), v_lds, vr[0]);
+    sstore(vs((r4 + 2) & 3), v_lds, vr[1]);
+    __syncthreads();
+    gload(kr[0], krs, (t + 5) * BN);
+    gload(kr[1], krs, (t + 6) * BN);
+    gload(vr[0], vrs, (t + 3) * BN);
+    gload(vr[1], vrs, (t + 4) * BN);
+  };
+  // Iteration flags: the first has no PV, the last no QK; only the one before the
+  // last may meet a partial tile (bidirectional).  Iterations t0 + i with i odd end a
+  // pair; the last one ends a pair too when i is odd, so that V(t1-1) is staged.
+  const long nt = t1 - t0;
+  if (nt == 1) {
     iteration(t0, Flag<false>{}, Flag<false>{}, Flag<false>{});
   } else {
     iteration(t0, Flag<false>{}, Flag<true>{}, Flag<true>{});
-    for (long t = t0 + 1; t + 2 < t1; ++t) iteration(t, Flag<true>{}, Flag<true>{}, Flag<false>{});
-    if (t1 - t0 > 2) iteration(t1 - 2, Flag<true>{}, Flag<true>{}, Flag<true>{});
-    iteration(t1 - 1, Flag<true>{}, Flag<false>{}, Flag<false>{});
+    long i = 1;
+    for (; i + 4 <= nt; i += 2) {  // iterations i and i+1 <= nt-3
+      iteration(t0 + i, Flag<true>{}, Flag<true>{}, Flag<false>{});
+      pair_end(t0 + i - 1);
+      iteration(t0 + i + 1, Flag<true>{}, Flag<true>{}, Flag<false>{});
+    }
+    // the remaining one to three iterations i .. nt-1
+    if (i == nt - 3) {
+      iteration(t0 + i, Flag<true>{}, Flag<true>{}, Flag<false>{});
+      if (i & 1) pair_end(t0 + i - 1);
+      ++i;
+    }
+    if (i == nt - 2) {
+      iteration(t0 + i, Flag<true>{}, Flag<true>{}, Flag<true>{});
+      if (i & 1) pair_end(t0 + i - 1);
+      ++i;
+    }
+    iteration(t0 + i, Flag<true>{}, Flag<false>{}, Flag<false>{});
+    if (i & 1) pair_end(t0 + i - 1);
   }
   {
-    const uint16_t* vt = vs((t1 - 1 - t0) & 1);
+    const uint16_t* vt = vs((t1 - 1 - t0) & 3);
 #pragma unroll
     for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
@@ -455,8 +494,8 @@ __device__ __forceinline__ void attend_segment(const AttnArgs& a, uint16_t* ks_b
 
 template <int HD>
 __global__ __launch_bounds__(64 * attn_waves<HD>(), attn_min_blocks<HD>()) void attention_kernel(AttnArgs a) {
-  __shared__ __align__(16) uint16_t ks[2 * kAttnBN * (HD + 8)];
-  __shared__ __align__(16) uint16_t vs[2 * kAttnBN * (HD + 32)];
+  __shared__ __align__(16) uint16_t ks[4 * kAttnBN * (HD + 8)];
+  __shared__ __align__(16) uint16_t vs[4 * kAttnBN * (HD + 32)];
   const long n_qt = (a.n_q + attn_rows<HD>() - 1) / attn_rows<HD>();
   const long tile = xcd_remap(blockIdx.x, n_qt * a.heads);
   attend_segment<HD>(a, ks, vs, tile, 0, (a.n_kv + kAttnBN - 1) / kAttnBN, nullptr);
@@ -470,8 +509,8 @@ __global__ __launch_bounds__(64 * attn_waves<HD>(), attn_min_blocks<HD>()) void 
 // order of the bidirectional kernel one XCD got far more work than another).
 template <int HD>
 __global__ __launch_bounds__(64 * attn_waves<HD>(), attn_min_blocks<HD>()) void attention_causal_kernel(AttnArgs a) {
-  __shared__ __align__(16) uint16_t ks[2 * kAttnBN * (HD + 8)];
-  __shared__ __align__(16) uint16_t vs[2 * kAttnBN * (HD + 32)];
+  __shared__ __align__(16) uint16_t ks[4 * kAttnBN * (HD + 8)];
+  __shared__ __align__(16) uint16_t vs[4 * kAttnBN * (HD + 32)];
   const long n_qt = (a.n_q + attn_rows<HD>() - 1) / attn_rows<HD>();
   const long b = blockIdx.x;
   const long tile = (b % a.heads) * n_qt + (n_qt - 1 - b / a.heads);
@@ -490,8 +529,8 @@ template <int HD>
 __global__ __launch_bounds__(64 * attn_waves<HD>(), attn_min_blocks<HD>()) void attention_split_kernel(AttnArgs a, float* ws,
                                                                                    long full, long tail,
                                                                                    int kp) {
-  __shared__ __align__(16) uint16_t ks[2 * kAttnBN * (HD + 8)];
-  __shared__ __align__(16) uint16_t vs[2 * kAttnBN * (HD + 32)];
+  __shared__ __align__(16) uint16_t ks[4 * kAttnBN * (HD + 8)];
+  __shared__ __align__(16) uint16_t vs[4 * kAttnBN * (HD + 32)];
   const long n_t = (a.n_kv + kAttnBN - 1) / kAttnBN;
   const long b = blockIdx.x;
   if (b < full) {
