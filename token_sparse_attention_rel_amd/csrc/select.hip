@@ -291,39 +291,44 @@ __global__ __launch_bounds__(kSelThreads) void select_compact_kernel(
     int krem = k;
     // Pad entries past n carry key 0; they are taken out of bin 0 while the prefix is 0.
     const uint32_t n_pad = static_cast<uint32_t>(n_chunks * kSelChunk - nl);
-    // histogram of digit `shift` over the keys of one run that match the prefix
-    auto hist_run = [&](const uint32_t (&key)[kSelRun], int shift) {
-      if (shift == 24) {
-        // first digit, every key takes part: one increment per wave when the digits
-        // agree (scores of one magnitude), per-lane LDS atomics otherwise
-#pragma unroll
-        for (int e = 0; e < kSelRun; ++e) {
-          const uint32_t d = key[e] >> 24;
-          const uint32_t d0 = __builtin_amdgcn_readfirstlane(d);
-          if (__ballot(d != d0) == 0) {
-            if (lane == 0) atomicAdd(&sh.hist[d0], 64u);
-          } else {
-            atomicAdd(&sh.hist[d], 1u);
-          }
-        }
+    // Histogram of digit `shift` over the keys that match the prefix.  In the first
+    // pass every key takes part and a thread's keys are consecutive tokens: equal
+    // digits in a row are added as one count (scores of similar size share their
+    // leading digits), so fewer lanes contend for one bin.  Later passes count the
+    // few keys under the prefix with one increment each.
+    uint32_t run_d = 0, run_n = 0;
+    auto count_key = [&](uint32_t key, int shift, bool merge) {
+      if ((key & pmask) != prefix) return;
+      const uint32_t d = (key >> shift) & 255u;
+      if (!merge) {
+        atomicAdd(&sh.hist[d], 1u);
+      } else if (d != run_d) {
+        if (run_n) atomicAdd(&sh.hist[run_d], run_n);
+        run_d = d;
+        run_n = 1;
       } else {
-#pragma unroll
-        for (int e = 0; e < kSelRun; ++e) {
-          if ((key[e] & pmask) == prefix) atomicAdd(&sh.hist[(key[e] >> shift) & 255u], 1u);
-        }
+        ++run_n;
       }
     };
     for (int shift = start; shift >= 0; shift -= 8) {
       if (tid < 256) sh.hist[tid] = 0;
       __syncthreads();
-      hist_run(v0, shift);
+      const bool merge = shift == start;
+      if (merge) {
+#pragma unroll
+        for (int e = 0; e < kSelRun; ++e) count_key(v0[e], shift, true);
+      } else {
+#pragma unroll
+        for (int e = 0; e < kSelRun; ++e) count_key(v0[e], shift, false);
+      }
       for (long i = kSelChunk + 4L * tid; i < end; i += 4L * kSelThreads) {
         uint32_t key[4];
         stream_keys(i, key);  // pads past n carry key 0 like those of the first chunk
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if ((key[e] & pmask) == prefix) atomicAdd(&sh.hist[(key[e] >> shift) & 255u], 1u);
+        for (int e = 0; e < 4; ++e) count_key(key[e], shift, merge);
       }
+      if (run_n) atomicAdd(&sh.hist[run_d], run_n);
+      run_n = 0;
       __syncthreads();
       if (wave == 0) {
         // lane owns bins 4*lane .. 4*lane+3; find the bin where the running count
