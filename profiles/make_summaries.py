@@ -4,7 +4,7 @@ Usage (repository root, after the GPU runs listed in each summary wrote gpurun_o
     python profiles/make_summaries.py gpurun_out
 Reads <dir>/prof_trace/run_kernel_trace.csv + run_kernel_stats.csv + prof_trace.log (the
 bench JSON line printed under the profiler), <dir>/pmc_{fetch,write,copy_fetch,copy_write} and
-<dir>/pmc_clock.
+<dir>/pmc_clock, and <dir>/prof_hbm (the standalone HBM-bound steps).
 """
 
 from __future__ import annotations
@@ -158,6 +158,36 @@ def stats_summary(d, sub, title, command):
     return "\n".join(out) + "\n"
 
 
+def hbm_summary(d):
+    """Kernel durations of the standalone HBM-bound steps (the bench's flushed repetitions)."""
+    trace = list(csv.DictReader(open(os.path.join(d, "prof_hbm", "run_kernel_trace.csv"))))
+    n, dim, k = 32760, 1536, 9828
+    kernels = [
+        ("a1 score", "score_kernel<", 2 * n * dim * 2 + 4 * n),
+        ("a4 gather", "gather_rows_kernel<false", k * dim * 4),
+        ("a6 cache sync", "copy_rows_kernel<true", 4 * k * dim * 2),
+        ("a8 scatter", "copy_rows_kernel<false", 2 * k * dim * 2),
+    ]
+    out = ["# rocprofv3 kernel-trace summary: HBM-bound steps alone, wan13b workload",
+           "# (N=32760, D=1536, 9828 active rows; the 256 MB MALL flushed before each repetition)",
+           "# command (repository root, one MI355X):",
+           "#   rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_hbm -o run -- \\",
+           "#       python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-dense",
+           "# summary written by: python profiles/make_summaries.py gpurun_out",
+           "# median kernel time of the last 20 dispatches (the bench's flushed repetitions),",
+           "# algorithmic bytes as in bench.py, against 8000 GB/s", "",
+           f"{'step':14s} {'kernel':40s} {'median_us':>10s} {'GB/s':>8s} {'frac':>6s}"]
+    for label, key, nbytes in kernels:
+        durs = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in trace if key in r["Kernel_Name"]]
+        if not durs:
+            continue
+        last = sorted(durs[-20:])
+        med = last[len(last) // 2] / 1e3
+        name = _short([r["Kernel_Name"] for r in trace if key in r["Kernel_Name"]][0])
+        out.append(f"{label:14s} {name[:40]:40s} {med:10.1f} {nbytes / med / 1e3:8.1f} {nbytes / med / 1e3 / 8000:6.3f}")
+    return "\n".join(out) + "\n"
+
+
 EXTRA = [
     ("prof_hsa_loop", "hsa_loop_wan13b_kernel_trace.txt",
      "HSA sampling loop (Euler update, phase window), N=32760, D=1536, 12 x 128, T=8",
@@ -187,6 +217,8 @@ def main(argv):
     open(os.path.join(here, "attention_wan13b_traffic.txt"), "w").write(traffic_summary(d))
     if glob.glob(os.path.join(d, "pmc_clock", "*counter_collection.csv")):
         open(os.path.join(here, "attention_wan13b_clock.txt"), "w").write(clock_summary(d))
+    if os.path.exists(os.path.join(d, "prof_hbm", "run_kernel_trace.csv")):
+        open(os.path.join(here, "hbm_kernels_wan13b_kernel_trace.txt"), "w").write(hbm_summary(d))
     for sub, fname, title, cmd in EXTRA:
         if os.path.exists(os.path.join(d, sub, "run_kernel_stats.csv")):
             open(os.path.join(here, fname), "w").write(stats_summary(d, sub, title, cmd))
