@@ -442,6 +442,32 @@ def test_attention_matches_oracle(n_q, n_kv, heads, hd):
     assert np.max(np.abs(G.host64(lse) - want_lse)) <= 1e-3 * max(1.0, np.abs(want_lse).max())
 
 
+@pytest.mark.slow
+def test_attention_at_the_buffer_range_limit():
+    """The largest K/V the ABI accepts for one head of 128: n_kv * 128 * 2 bytes just under
+    2**31 (8388607 keys, 2 GiB each for K and V), so the 32-bit buffer offsets of the K/V
+    loads and the range check of the prefetches past the last key run at their limit.
+    Whole tiles and the split schedule, sampled query rows against the oracle."""
+    t = tsa()
+    heads, hd = 1, 128
+    n_kv = (2 ** 31 - 1) // (heads * hd * 2)
+    n_q = 300
+    gen = torch.Generator(device="cuda").manual_seed(31)
+    q = (3.0 * torch.randn(n_q, hd, device="cuda", generator=gen)).to(torch.bfloat16)
+    k = torch.randn(n_kv, hd, device="cuda", generator=gen).to(torch.bfloat16)
+    v = torch.randn(n_kv, hd, device="cuda", generator=gen).to(torch.bfloat16)
+    rows = np.array([0, 1, 150, 255, 256, 299])
+    print(f"  n_kv={n_kv} ({n_kv * hd * 2} bytes per cache); oracle on rows {rows.tolist()}", flush=True)
+    want = ref.attention(G.host64(q)[rows], G.host64(k), G.host64(v), heads)
+    ws_bytes = t.attention_workspace_bytes(n_q, n_kv, heads, hd)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    for name, w in (("whole tiles", None), ("split", ws if ws_bytes > 0 else None)):
+        out = torch.empty(n_q, hd, dtype=torch.bfloat16, device="cuda")
+        t.sparse_query_attention(q, k, v, n_q, heads, hd, out, workspace=w)
+        torch.cuda.synchronize()
+        G.assert_close(G.host64(out)[rows], want, f"attention at the range limit, {name}")
+
+
 # Split schedule: shapes whose last round of query tiles (256 queries for head_dim 128, 128
 # for 64) leaves a 256-CU GPU partly idle, ragged in queries and keys, so that tiles are cut
 # into key ranges and merged; fewer tiles than compute units (all tiles cut), tails of
