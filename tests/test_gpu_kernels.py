@@ -340,6 +340,61 @@ def test_qkv_matches_oracle(n_x, m, dim, src):
     assert torch.equal(kch[rows], k.cpu()) and torch.equal(vch[rows], v.cpu())
 
 
+@pytest.mark.slow
+@pytest.mark.parametrize("src", ["bf16", "recover"])
+def test_qkv_at_the_buffer_range_limit(src):
+    """Token rows at the end of the largest input the ABI accepts (n_x * dim * 2 bytes just
+    under 2**31, 699050 rows of 1536): the 32-bit offsets of the row loads (and of the noise
+    rows) run at their limit; K/V written into caches of the same size."""
+    t = tsa()
+    dim = 1536
+    n_x = (2 ** 31 - 1) // (dim * 2)
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    x = torch.randn(n_x, dim, device="cuda", generator=gen).to(torch.bfloat16)
+    w = (torch.randn(3 * dim, dim, device="cuda", generator=gen) / math.sqrt(dim)).to(torch.bfloat16)
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([np.arange(16), np.arange(n_x - 300, n_x),
+                                     rng.choice(n_x, 700, replace=False)])).astype(np.int32)
+    m = rows.size
+    rd = G.dev(torch.from_numpy(rows))
+    q = torch.empty(m, dim, dtype=torch.bfloat16, device="cuda")
+    k = torch.empty_like(q)
+    v = torch.empty_like(q)
+    kc = torch.zeros(n_x, dim, dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    x_rows = G.host64(x[torch.from_numpy(rows).long().cuda()])
+    if src == "recover":
+        eps = torch.randn(n_x, dim, device="cuda", generator=gen).to(torch.bfloat16)
+        off, sigma = 3600, 0.6
+        kw = dict(eps=eps, src_row_offset=off, sigma=sigma)
+        # the recovery rows of the sampled tokens, from the gathered clean and noise rows
+        srcr = rows.astype(np.int64) - off
+        ok = srcr >= 0
+        clean = np.zeros((m, dim))
+        clean[ok] = G.host64(x[torch.from_numpy(srcr[ok]).cuda()])
+        a_rows = ref.recover_rows(clean, G.host64(eps[torch.from_numpy(rows).long().cuda()]), np.arange(m), 0, sigma)
+    else:
+        kw = {}
+        a_rows = x_rows
+    t.qkv_active(x, rd, m, w, q_out=q, k_out=k, v_out=v, **kw)
+    t.qkv_active(x, rd, m, w, k_out=kc, v_out=vc, out_is_cache=True, n_cache=n_x, **kw)
+    torch.cuda.synchronize()
+    want = ref.project(a_rows, G.host64(w))
+    for name, got in (("q", q), ("k", k), ("v", v)):
+        gh = G.host64(got)
+        if src == "recover":
+            G.assert_close(gh, want[name], f"range limit {src} {name}")
+        else:
+            part = "qkv".index(name)
+            wp = np.abs(G.host64(w)[part * dim:(part + 1) * dim])
+            G.assert_projection_close(gh, want[name], np.abs(ref.round_bf16(a_rows)) @ wp.T, dim,
+                                      f"range limit {src} {name}")
+    rl = torch.from_numpy(rows).long().cuda()
+    assert torch.equal(kc[rl], k) and torch.equal(vc[rl], v)
+    others = torch.from_numpy(np.setdiff1d(rng.choice(n_x, 2000, replace=False), rows)).long().cuda()
+    assert not kc[others].any() and not vc[others].any()
+
+
 @pytest.mark.parametrize("src", ["bf16", "recover", "f32"])
 def test_qkv_large_tile_sampled(src):
     """A grid of at least 1024 256x256 tiles takes the large-tile kernel: checked on sampled
