@@ -120,6 +120,40 @@ def test_fused_and_unfused_paths_bit_identical():
         assert torch.equal(a, b)
 
 
+def test_concurrent_streams_match_sequential_steps():
+    """The library keeps no per-call state: two layers stepping at the same time on two
+    streams (default priority) give the bits they give one after the other, with the split
+    attention schedule and its workspace on both."""
+    t = tsa()
+    cfgs = [scaled(configs.get_config("wan13b"), frames=3, height=20, width=52),
+            scaled(configs.get_config("wan13b"), frames=2, height=30, width=40)]
+    layers, xs = [], []
+    for i, cfg in enumerate(cfgs):
+        inp = generate.step_inputs(cfg, i)
+        layers.append(t.PrunedAttentionLayer(cfg.n, cfg.dim, cfg.heads, G.dev(inp["w_qkv"]),
+                                             split_attention=True))
+        xs.append((G.dev(inp["x_prev"]), G.dev(inp["x_cur"])))
+
+    def run(streams):
+        outs = []
+        for layer, (xp, xc), cfg, st in zip(layers, xs, cfgs, streams):
+            with torch.cuda.stream(st):
+                layer.init_cache(xp)
+                for _ in range(3):
+                    layer.step_topk(xc, xp, cfg.n_active)
+        torch.cuda.synchronize()
+        for layer in layers:
+            outs.append((layer.out.clone(), layer.k_cache.clone(), layer.idx.clone(), layer.mask.clone()))
+        return outs
+
+    cur = torch.cuda.current_stream()
+    seq = run([cur, cur])
+    par = run([torch.cuda.Stream(), torch.cuda.Stream()])
+    for a, b in zip(seq, par):
+        for x, y in zip(a, b):
+            assert torch.equal(x, y)
+
+
 def test_threshold_step_zero_change_leaves_state():
     t = tsa()
     cfg = scaled(configs.get_config("wan13b"), frames=2, height=10, width=16)
