@@ -68,6 +68,37 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Data-parallel-primitive moves inside a row of 16 lanes (quad_perm 1,0,3,2 and
+// 2,3,0,1, half-row mirror, row mirror): summing a value with each in turn leaves
+// every lane of an aligned group of 4, 8 or 16 lanes holding the group's sum.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+template <int L>
+__device__ __forceinline__ float lane_group_sum(float v) {
+  static_assert(L == 4 || L == 8 || L == 16, "lane groups of 4, 8 or 16");
+  v += dpp_move<0xB1>(v);  // quad_perm [1, 0, 3, 2]
+  v += dpp_move<0x4E>(v);  // quad_perm [2, 3, 0, 1]
+  if constexpr (L >= 8) v += dpp_move<0x141>(v);   // row_half_mirror: lane i <-> 7 - i
+  if constexpr (L >= 16) v += dpp_move<0x140>(v);  // row_mirror: lane i <-> 15 - i
+  return v;
+}
+
+// Sum over the 64 lanes of a wave in a fixed order without LDS: the four rows of
+// 16 lanes by DPP moves, then the row sums (lanes 0, 16, 32, 48) read out and added
+// in row order.  The result is wave-uniform.
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v = lane_group_sum<16>(v);
+  const int b = __float_as_int(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(b, 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(b, 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(b, 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(b, 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
 // Number of set lanes of a 64-bit ballot below the calling lane.
 __device__ __forceinline__ int lanes_below(uint64_t ballot) {
   return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(ballot >> 32),

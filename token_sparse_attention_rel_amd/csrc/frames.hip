@@ -214,10 +214,136 @@ __global__ __launch_bounds__(kLifThreads) void lif_mask_kernel(const T* __restri
   if (f + 2 < frames) step(f + 2, S3{});
 }
 
+// Rows of up to 64 * kLifWaveMaxCpt slices: one wave per spatial location (four per
+// 256-thread workgroup).  Lane l holds slices l + 64 j (j < CPT) of each row as raw
+// 16-byte slices: frame f sits in ring slot f mod 3, so the previous frame is the slot
+// before it and the frame two ahead is fetched into the previous frame's slot once it is
+// used; the last kept row and the sums of magnitudes of the previous and the kept row
+// (the denominators of the relative scores) are carried along.  Sums cross the wave by
+// DPP moves and four lane reads in a fixed order: no LDS, no barrier between frames.
+constexpr int kLifWaveMaxCpt = 6;
+
+template <typename T, int CPT>
+__global__ __launch_bounds__(256) void lif_mask_wave_kernel(const T* __restrict__ x, long frames, long hw,
+                                                            long dim, int relative, float tau_s, float tau_l,
+                                                            uint8_t* __restrict__ mask,
+                                                            float* __restrict__ short_out,
+                                                            float* __restrict__ long_out) {
+  constexpr int V = Slice<T>::kVec;
+  const long loc = static_cast<long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (loc >= hw) return;  // a whole wave
+  const int lane = threadIdx.x & 63;
+  const long n_sl = dim / V;
+  // slices past the row end read the last slice (no branch around the load) and count as zero
+  auto load_raw = [&](u32x4 (&dst)[CPT], long f) {
+    const T* row = x + (f * hw + loc) * dim;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const long sl = lane + 64L * j;
+      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + (sl < n_sl ? sl : n_sl - 1) * V));
+      dst[j] = sl < n_sl ? v : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  u32x4 ring[3][CPT], ref[CPT];
+  load_raw(ring[0], 0);
+  if (1 < frames) load_raw(ring[1], 1);
+  if (2 < frames) load_raw(ring[2], 2);
+  float den_prev = 0.f;  // sum |x| of the previous row
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+    float p[V];
+    Slice<T>::unpack(ring[0][j], p);
+#pragma unroll
+    for (int e = 0; e < V; ++e) den_prev += fabsf(p[e]);
+    ref[j] = ring[0][j];
+  }
+  den_prev = wave_sum_dpp(den_prev);
+  float den_ref = den_prev;  // sum |x| of the last kept row
+  if (lane == 0) {
+    mask[loc] = 1;
+    if (short_out) short_out[loc] = __builtin_inff();
+    if (long_out) long_out[loc] = __builtin_inff();
+  }
+  auto step = [&](long f, auto cur_c, auto tail_c) {
+    constexpr int sc = decltype(cur_c)::value, sp = (sc + 2) % 3;  // slots of frames f and f - 1
+    float num_s = 0.f, num_l = 0.f, den_c = 0.f;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      float c[V], p[V], r[V];
+      // unpack the previous row again rather than keep last step's fp32 copy of it live
+      // (an empty asm hides that the two are equal): three raw rows fit the registers,
+      // three fp32 rows do not
+      u32x4 pr = ring[sp][j], rr = ref[j];
+      asm volatile("" : "+v"(pr), "+v"(rr));
+      Slice<T>::unpack(ring[sc][j], c);
+      Slice<T>::unpack(pr, p);
+      Slice<T>::unpack(rr, r);
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        num_s += fabsf(c[e] - p[e]);
+        num_l += fabsf(c[e] - r[e]);
+        den_c += fabsf(c[e]);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // one slice at a time
+    }
+    // frame f - 1 is no longer needed: fetch frame f + 2 into its slot (inside the main
+    // loop it always exists; a conditional fetch there would keep the old row live too)
+    if (!decltype(tail_c)::value || f + 2 < frames) load_raw(ring[sp], f + 2);
+    num_s = wave_sum_dpp(num_s);
+    num_l = wave_sum_dpp(num_l);
+    den_c = wave_sum_dpp(den_c);
+    const float ss = l1_score(num_s, den_prev, relative);
+    const float ls = l1_score(num_l, den_ref, relative);
+    // the sums are wave-uniform, so is the decision: say so, and the row update is a branch
+    const bool keep = __builtin_amdgcn_readfirstlane(!((ss < tau_s) && (ls < tau_l)) ? 1 : 0) != 0;
+    const long t = f * hw + loc;
+    if (lane == 0) {
+      mask[t] = keep ? 1 : 0;
+      if (short_out) short_out[t] = ss;
+      if (long_out) long_out[t] = ls;
+    }
+    if (keep) {
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) ref[j] = ring[sc][j];
+      den_ref = den_c;
+    }
+    den_prev = den_c;
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using Main = std::false_type;
+  using Tail = std::true_type;
+  long f = 1;
+  for (; f + 4 < frames; f += 3) {  // fetches up to frame f + 4
+    step(f, S1{}, Main{});
+    step(f + 1, S2{}, Main{});
+    step(f + 2, S0{}, Main{});
+  }
+  // at most four frames left
+  if (f < frames) step(f, S1{}, Tail{});
+  if (f + 1 < frames) step(f + 1, S2{}, Tail{});
+  if (f + 2 < frames) step(f + 2, S0{}, Tail{});
+  if (f + 3 < frames) step(f + 3, S1{}, Tail{});
+}
+
 template <typename T>
 hipError_t launch_lif_t(const T* x, long frames, long hw, long dim, int relative, float tau_s, float tau_l,
                         uint8_t* mask, float* so, float* lo, hipStream_t s) {
-  const long cpt = (dim / Slice<T>::kVec + kLifThreads - 1) / kLifThreads;
+  const long n_sl = dim / Slice<T>::kVec;
+  const long wcpt = (n_sl + 63) / 64;  // slices per lane with one wave per location
+  if (wcpt <= kLifWaveMaxCpt) {
+    const dim3 wgrid(static_cast<unsigned>((hw + 3) / 4)), wblock(256);
+    switch (wcpt <= 2 ? wcpt : (wcpt <= 4 ? 4 : kLifWaveMaxCpt)) {
+      case 1: hipLaunchKernelGGL((lif_mask_wave_kernel<T, 1>), wgrid, wblock, 0, s, x, frames, hw, dim, relative, tau_s, tau_l, mask, so, lo); break;
+      case 2: hipLaunchKernelGGL((lif_mask_wave_kernel<T, 2>), wgrid, wblock, 0, s, x, frames, hw, dim, relative, tau_s, tau_l, mask, so, lo); break;
+      case 4: hipLaunchKernelGGL((lif_mask_wave_kernel<T, 4>), wgrid, wblock, 0, s, x, frames, hw, dim, relative, tau_s, tau_l, mask, so, lo); break;
+      default: hipLaunchKernelGGL((lif_mask_wave_kernel<T, kLifWaveMaxCpt>), wgrid, wblock, 0, s, x, frames, hw, dim, relative, tau_s, tau_l, mask, so, lo); break;
+    }
+    return hipGetLastError();
+  }
+  // longer rows: one workgroup per location
+  const long cpt = (n_sl + kLifThreads - 1) / kLifThreads;
   const dim3 grid(static_cast<unsigned>(hw)), block(kLifThreads);
   switch (cpt) {
     case 1: hipLaunchKernelGGL((lif_mask_kernel<T, 1>), grid, block, 0, s, x, frames, hw, dim, relative, tau_s, tau_l, mask, so, lo); break;

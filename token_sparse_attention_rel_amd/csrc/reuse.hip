@@ -51,23 +51,6 @@ __device__ __forceinline__ void axis_back3(const ReuseGeom& g, uint32_t t, long 
   nb[2] = in_frame % w ? static_cast<long>(t) - 1 : -1;
 }
 
-// Data-parallel-primitive moves inside a row of 16 lanes (quad_perm 1,0,3,2 and
-// 2,3,0,1, half-row mirror, row mirror): summing a value with each in turn leaves
-// every lane of an aligned group of 4, 8 or 16 lanes holding the group's sum.
-template <int CTRL>
-__device__ __forceinline__ float dpp_move(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-
-template <int L>
-__device__ __forceinline__ float lane_group_sum(float v) {
-  v += dpp_move<0xB1>(v);  // quad_perm [1, 0, 3, 2]
-  v += dpp_move<0x4E>(v);  // quad_perm [2, 3, 0, 1]
-  if constexpr (L >= 8) v += dpp_move<0x141>(v);   // row_half_mirror: lane i <-> 7 - i
-  if constexpr (L >= 16) v += dpp_move<0x140>(v);  // row_mirror: lane i <-> 15 - i
-  return v;
-}
-
 template <int HD>
 __global__ __launch_bounds__(256) void reuse_delta_src_kernel(const uint16_t* __restrict__ v, ReuseGeom geo,
                                                               float th0, float th1, float th2,
