@@ -497,6 +497,37 @@ def test_attention_matches_oracle(n_q, n_kv, heads, hd):
     assert np.max(np.abs(G.host64(lse) - want_lse)) <= 1e-3 * max(1.0, np.abs(want_lse).max())
 
 
+@pytest.mark.parametrize("hd", [128, 64])
+def test_attention_every_tile_count_up_to_40(hd):
+    """K/V tiles (32 keys) are staged two per barrier, with the loop's first, last and
+    next-to-last iterations specialised: every cache length from one tile to 40 tiles, whole
+    and ragged, for both head widths, against the oracle (and the split schedule too)."""
+    t = tsa()
+    heads, n_q = 2, 70
+    dim = heads * hd
+    g = torch.Generator().manual_seed(hd)
+    lengths = sorted({1, 2, 31, 32, 33} | {32 * nt + r for nt in range(1, 41) for r in (0, 7)})
+    k_all = _randn_bf16(g, max(lengths), dim)
+    v_all = _randn_bf16(g, max(lengths), dim)
+    q = _randn_bf16(g, n_q, dim, scale=2.0)
+    qd = G.dev(q)
+    for n_kv in lengths:
+        kd, vd = G.dev(k_all[:n_kv]), G.dev(v_all[:n_kv])
+        want = ref.attention(G.host64(q), G.host64(k_all[:n_kv]), G.host64(v_all[:n_kv]), heads)
+        out = torch.empty(n_q, dim, dtype=torch.bfloat16, device="cuda")
+        t.sparse_query_attention(qd, kd, vd, n_q, heads, hd, out)
+        got = G.host64(out)
+        ws_bytes = t.attention_workspace_bytes(n_q, n_kv, heads, hd)
+        if ws_bytes:
+            ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+            out2 = torch.empty_like(out)
+            t.sparse_query_attention(qd, kd, vd, n_q, heads, hd, out2, workspace=ws)
+            G.assert_close(G.host64(out2), want, f"split n_kv={n_kv} d={hd}")
+        assert G.rel_frob(got, want) <= G.REL_FROB, n_kv
+        assert np.max(np.abs(got - want) / np.maximum(1.0, np.abs(want))) <= G.MAX_ABS, n_kv
+    print(f"  {len(lengths)} cache lengths from {lengths[0]} to {lengths[-1]} keys", flush=True)
+
+
 @pytest.mark.slow
 def test_attention_at_the_buffer_range_limit():
     """The largest K/V the ABI accepts for one head of 128: n_kv * 128 * 2 bytes just under
