@@ -241,7 +241,7 @@ def hbm_kernels(tsa, torch, cfg, layer, xc, xp, reps=20):
 
 def bench_step(args, torch, tsa, cfg):
     """One pruned layer step (score + top-k + compaction, QKV + cache sync, attention +
-    scatter), K timed steps; the driver's JSON line for the headline workload."""
+    scatter), K timed steps; the JSON line of the headline workload."""
     from workloads import generate
 
     dev = torch.device("cuda:0")
