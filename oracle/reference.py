@@ -450,8 +450,8 @@ def rope3d(x_rows, tokens, height: int, width: int, heads: int, base: float = 10
     head's channels into a temporal group and two spatial groups (x and y); LIPAR page §2.C
     requires the pruned path to respect those rotations.  Q and K are rotated by their own
     tokens' positions.  Each head's channels are split into time / height / width groups
-    (rope_split, the group sizes being this build's reading); inside the group of axis a,
-    of size d_a, the channel pair
+    (rope_split; the page gives no group sizes, so these are a reading of it); inside the
+    group of axis a, of size d_a, the channel pair
     (2i, 2i+1), read as the complex number x_2i + i x_2i+1, is multiplied by
     exp(i p_a base^(-2i/d_a)), p_a being the token's coordinate along a.  Float64, not rounded.
     """
