@@ -11,7 +11,8 @@ TFLOP/s = 4 * N_active * N * head_dim * heads / step time.  Extra fields give
 tokens/s, the per-kernel times (median / p10 / p90 over the timed steps), the
 attention kernel's roofline, the HBM-bound steps timed standalone against the
 HBM peak, the dense layer and the CPU oracle measured on a bounded sample of
-the same workload.
+the same workload.  Step labels (a1 score ... a8 scatter) follow
+include/tsa.h.
 
 Other workloads (``--workload``): ``large`` and ``tiny`` (the same step),
 ``hsa`` (the T-step schedule loop), ``hsa_loop`` (the sampling loop with the

@@ -5,6 +5,13 @@
  *   score -> select -> compact -> QKV of the active tokens -> KV-cache sync
  *   -> attention of the active queries over the whole cache -> scatter.
  *
+ * Step labels used in the comments below:
+ *   a1 score, a2 select, a3 compact, a4 gather (optionally with recovery),
+ *   a5 QKV projection, a6 KV-cache sync, a7 attention, a8 scatter;
+ *   f1 cached Euler update, f2 long/short-term pruning mask and frame
+ *   restoration, f3 3D rotary positions and frame-causal attention,
+ *   f4 Timeripple partial-score reuse (the steps beside the layer).
+ *
  * Sources, cited by page title and section (gist.science summaries):
  *   [HSA]   "Resumen Técnico: Asignación de Pasos Heterogénea (HSA) para la
  *           Generación Eficiente de Video", gist.science/es/paper/2605.06892

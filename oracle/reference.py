@@ -3,6 +3,12 @@
 TEST INFRASTRUCTURE ONLY (see the package docstring): slow, obviously
 correct, one function per step, in the order the method runs them.
 
+Step labels in the section headers: a1 score, a2 select, a3 compact,
+a4 gather / recovery rows, a5 projection, a6 cache sync, a7 attention,
+a8 scatter; f1 cached Euler update, f2 long/short-term pruning mask and
+restoration, f3 3D rotary positions and frame-causal attention, f4
+Timeripple partial-score reuse.
+
 Conventions
 -----------
 * Token rows are row-major ``[N, D]``; inside Q/K/V, column ``h*d + j`` is

@@ -4,6 +4,11 @@ The compute path is libtsa.so (include/tsa.h); this package only loads it,
 marshals arguments (``_binding``) and sequences the calls of one layer step
 (``layer``).  Importing the package loads the library and raises if it has
 not been built: there is no CPU fallback.
+
+Docstrings label the steps as include/tsa.h does: a1 score, a2 select,
+a3 compact, a4 gather, a5 QKV projection, a6 KV-cache sync, a7 attention,
+a8 scatter; f1-f4 are the steps beside the layer (Euler update, pruning
+mask and restoration, rotary frame-causal attention, Timeripple reuse).
 """
 
 from . import _binding
