@@ -20,10 +20,13 @@
 // Tile: 256 output features x 256 tokens x 64 (K) per step, 8 waves in a 4x2
 // arrangement, each wave 64 features x 128 tokens (2 x 4 MFMA blocks): six
 // 16-byte LDS reads feed eight MFMAs, and each staged K slice is shared by 256
-// columns and 256 tokens.  Two LDS buffers (144 KB, one workgroup per CU, one
-// barrier per K step); the registers prefetch the K step after next while the
-// current one is multiplied.  Grids of fewer than four such tiles per CU use
-// 128 x 128 tiles on 4 waves instead (two workgroups per CU).  bf16 rows (and the recovery noise) arrive through
+// columns and 256 tokens.  Two LDS buffers, one barrier per K step.  Grids of
+// fewer than four such tiles per CU use 128 x 128 tiles on 4 waves instead (two
+// workgroups per CU).  On the large tile, bf16 rows are copied from HBM straight
+// into LDS (qkv_gemm_lds_kernel: no registers, the next K step's copy in flight
+// while the current one is multiplied); otherwise, and for rows that need
+// arithmetic on the way (the recovery blend, fp32 input), operands go through
+// registers, loaded two K steps ahead (qkv_gemm_kernel).  All rows arrive through
 // range-checked buffer loads (invalid rows read as zeros, no per-step selects).
 #include "common.h"
 #include "kernels.h"
@@ -120,6 +123,81 @@ constexpr int kOutOfRange = 0x7FFFFFF0;
 // time on one XCD then share few W panels and few token tiles in its L2.
 constexpr int kTokGroup = 4;
 
+// First output feature (absolute) and first compact token row of this workgroup's tile.
+// Tile order: XCD-aware, then groups of kTokGroup token tiles with the token tile
+// varying fastest, so concurrently running workgroups share W panels.
+template <typename TL>
+__device__ __forceinline__ void tile_origin(const GemmArgs& a, long& c_base, long& t_base) {
+  const long n_col = (a.ncols + TL::kBM - 1) / TL::kBM;
+  const long n_tok = (a.n + TL::kBN - 1) / TL::kBN;
+  const long L = xcd_remap(blockIdx.x, n_col * n_tok);
+  const long grp = L / (kTokGroup * n_col);
+  const long first_tok = grp * kTokGroup;
+  const long gsize = (n_tok - first_tok) < kTokGroup ? (n_tok - first_tok) : kTokGroup;
+  const long local = L - grp * kTokGroup * n_col;
+  const long tok_tile = first_tok + local % gsize;
+  const long col_tile = local / gsize;
+  c_base = a.col0 + col_tile * TL::kBM;
+  t_base = tok_tile * TL::kBN;
+}
+
+// Epilogue: lane holds token (l32) and features 8g + 4*(lane/32) + 0..3 of each 32-block.
+// Q goes to compact row r; K and V to compact row r or, fused cache sync, to the
+// token's cache row.  Optionally Q and K are rotated by the token's 3D position.
+template <typename TL>
+__device__ __forceinline__ void store_tile(const GemmArgs& a, const f32x16 (&acc)[TL::kBF][TL::kBT],
+                                           long c_base, long t_base, int wc, int wt, int lane) {
+  constexpr int kWaveBF = TL::kBF, kWaveBT = TL::kBT;
+  const long c_end = a.col0 + a.ncols;
+  const int l32 = lane & 31;
+  const int fsub = (lane >> 5) * 4;
+#pragma unroll
+  for (int j = 0; j < kWaveBT; ++j) {
+    const long r = t_base + (wt * kWaveBT + j) * 32 + l32;
+    if (r >= a.n) continue;
+    const long t = a.out_rows ? static_cast<long>(a.out_rows[r]) : r;
+    float pos[3] = {0.f, 0.f, 0.f};
+    if (a.rope_d) {
+      const unsigned tu = static_cast<unsigned>(t), hw = static_cast<unsigned>(a.rope_hw),
+                     w = static_cast<unsigned>(a.rope_w);
+      const unsigned in_frame = tu % hw;
+      pos[0] = static_cast<float>(tu / hw);
+      pos[1] = static_cast<float>(in_frame / w);
+      pos[2] = static_cast<float>(in_frame % w);
+    }
+#pragma unroll
+    for (int i = 0; i < kWaveBF; ++i) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const long c = c_base + (wc * kWaveBF + i) * 32 + g * 8 + fsub;
+        if (c >= c_end) continue;
+        const long part = c / a.dim;
+        const long cc = c - part * a.dim;
+        uint16_t* base;
+        long row;
+        if (part == 0) {
+          base = a.q;
+          row = r;
+        } else {
+          base = part == 1 ? a.k : a.v;
+          row = a.to_cache ? t : r;
+        }
+        float o[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+        if (a.rope_d && part < 2) {
+          const int hj = static_cast<int>(cc % a.rope_d);
+          rope_pair(a, pos, hj, o[0], o[1]);
+          rope_pair(a, pos, hj + 2, o[2], o[3]);
+        }
+        const u32x2 val{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+        *reinterpret_cast<u32x2*>(base + row * a.dim + cc) = val;
+      }
+    }
+  }
+}
+
+// Operand rows staged through registers, loaded two K steps ahead and stored to
+// padded LDS rows one step ahead (converted on the way for the recovery blend and
+// fp32 input).
 template <int SRC, typename TL>
 __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void qkv_gemm_kernel(GemmArgs a) {
   constexpr int kGemmBM = TL::kBM, kGemmBN = TL::kBN, kGemmWavesT = TL::kWavesT;
@@ -128,21 +206,9 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void qkv_gemm_kernel(
   __shared__ __align__(16) uint16_t ws[2][kGemmBM * kGemmLD];
   __shared__ __align__(16) uint16_t as[2][kGemmBN * kGemmLD];
 
-  // Tile order: XCD-aware, then groups of kTokGroup token tiles with the token
-  // tile varying fastest, so concurrently running workgroups share W panels.
-  const long n_col = (a.ncols + kGemmBM - 1) / kGemmBM;
-  const long n_tok = (a.n + kGemmBN - 1) / kGemmBN;
-  const long L = xcd_remap(blockIdx.x, n_col * n_tok);
-  const long grp = L / (kTokGroup * n_col);
-  const long first_tok = grp * kTokGroup;
-  const long gsize = (n_tok - first_tok) < kTokGroup ? (n_tok - first_tok) : kTokGroup;
-  const long local = L - grp * kTokGroup * n_col;
-  const long tok_tile = first_tok + local % gsize;
-  const long col_tile = local / gsize;
-
+  long c_base, t_base;
+  tile_origin<TL>(a, c_base, t_base);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const long c_base = a.col0 + col_tile * kGemmBM;  // absolute feature
-  const long t_base = tok_tile * kGemmBN;            // compact token row
   const long c_end = a.col0 + a.ncols;
 
   // Loader slots: rows lrow + kLoadRows*j of each tile, 16-byte chunk (tid & 7) of the K slice.
@@ -268,50 +334,121 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void qkv_gemm_kernel(
     if (ks + 2 < n_k) load_tiles((ks + 2) * kGemmBK);
   }
 
-  // Epilogue: lane holds token (l32) and features 8g + 4*(lane/32) + 0..3 of each 32-block.
-  const int fsub = (lane >> 5) * 4;
+  store_tile<TL>(a, acc, c_base, t_base, wc, wt, lane);
+}
+
+// One 16-byte piece per lane from a range-checked buffer straight into LDS: lane i
+// writes bytes 16i .. 16i+15 after `lds` (wave-uniform), no registers involved.
+__device__ __forceinline__ void lds_copy16(__amdgpu_buffer_rsrc_t rs, uint16_t* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+// Wait until every copy this wave issued has landed in LDS (vmcnt 0).
+__device__ __forceinline__ void lds_copy_wait() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// bf16 token rows, which need no conversion: the operand tiles go from HBM to LDS
+// without passing through registers.  LDS rows are unpadded (64 elements, 128 bytes);
+// 16-byte chunk c of row r sits at chunk c ^ ((r / 2) % 8), so the 16 rows that one
+// quarter-wave of a ds_read_b128 touches (one chunk column) fall on 16 distinct
+// 16-byte bank groups.  One copy instruction moves 8 rows (1 KB) of a tile; each K step
+// is copied into the buffer not being multiplied while the other one is, and every
+// buffer is an LDS array of its own, so the only waits for the copies are at the
+// barrier that ends the step.
+template <typename TL>
+__global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void qkv_gemm_lds_kernel(GemmArgs a) {
+  constexpr int kGemmBM = TL::kBM, kGemmBN = TL::kBN, kGemmWavesT = TL::kWavesT;
+  constexpr int kWaveBF = TL::kBF, kWaveBT = TL::kBT;
+  constexpr int kWaves = TL::kThreads / 64;
+  constexpr int kCopyW = kGemmBM / 8 / kWaves, kCopyA = kGemmBN / 8 / kWaves;  // copies per wave and step
+  static_assert(kCopyW * 8 * kWaves == kGemmBM && kCopyA * 8 * kWaves == kGemmBN, "8-row copies per wave");
+  __shared__ __align__(16) uint16_t ws0[kGemmBM * kGemmBK], ws1[kGemmBM * kGemmBK];
+  __shared__ __align__(16) uint16_t as0[kGemmBN * kGemmBK], as1[kGemmBN * kGemmBK];
+
+  long c_base, t_base;
+  tile_origin<TL>(a, c_base, t_base);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // LDS destinations in scalars
+  const long c_end = a.col0 + a.ncols;
+  const long dim = a.dim;
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.w), 0, static_cast<int>(3 * dim * dim * 2), kBufferRsrcFlags);
+  const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(a.x), 0, static_cast<int>(a.n_x_rows * dim * 2), kBufferRsrcFlags);
+  // Copy j of this wave: lane L fetches the logical chunk stored at physical chunk L % 8
+  // of tile row 8 * (wave * per + j) + L / 8; rows past the matrix read zeros.
+  int w_off[kCopyW], a_off[kCopyA];
 #pragma unroll
-  for (int j = 0; j < kWaveBT; ++j) {
-    const long r = t_base + (wt * kWaveBT + j) * 32 + l32;
-    if (r >= a.n) continue;
-    const long t = a.out_rows ? static_cast<long>(a.out_rows[r]) : r;
-    float pos[3] = {0.f, 0.f, 0.f};
-    if (a.rope_d) {
-      const unsigned tu = static_cast<unsigned>(t), hw = static_cast<unsigned>(a.rope_hw),
-                     w = static_cast<unsigned>(a.rope_w);
-      const unsigned in_frame = tu % hw;
-      pos[0] = static_cast<float>(tu / hw);
-      pos[1] = static_cast<float>(in_frame / w);
-      pos[2] = static_cast<float>(in_frame % w);
-    }
-#pragma unroll
-    for (int i = 0; i < kWaveBF; ++i) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const long c = c_base + (wc * kWaveBF + i) * 32 + g * 8 + fsub;
-        if (c >= c_end) continue;
-        const long part = c / a.dim;
-        const long cc = c - part * a.dim;
-        uint16_t* base;
-        long row;
-        if (part == 0) {
-          base = a.q;
-          row = r;
-        } else {
-          base = part == 1 ? a.k : a.v;
-          row = a.to_cache ? t : r;
-        }
-        float o[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-        if (a.rope_d && part < 2) {
-          const int hj = static_cast<int>(cc % a.rope_d);
-          rope_pair(a, pos, hj, o[0], o[1]);
-          rope_pair(a, pos, hj + 2, o[2], o[3]);
-        }
-        const u32x2 val{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-        *reinterpret_cast<u32x2*>(base + row * a.dim + cc) = val;
-      }
-    }
+  for (int j = 0; j < kCopyW; ++j) {
+    const int row = 8 * (wave_s * kCopyW + j) + (lane >> 3);
+    const int lc = (lane & 7) ^ ((row >> 1) & 7);
+    const long c = c_base + row;
+    w_off[j] = c < c_end ? static_cast<int>((c * dim + lc * 8) * 2) : kOutOfRange;
   }
+#pragma unroll
+  for (int j = 0; j < kCopyA; ++j) {
+    const int row = 8 * (wave_s * kCopyA + j) + (lane >> 3);
+    const int lc = (lane & 7) ^ ((row >> 1) & 7);
+    const long r = t_base + row;
+    const long tok = r < a.n ? (a.rows ? static_cast<long>(a.rows[r]) : r) : 0;
+    a_off[j] = r < a.n ? static_cast<int>((tok * dim + lc * 8) * 2) : kOutOfRange;
+  }
+  auto copy_step = [&](uint16_t* wbuf, uint16_t* abuf, long k0) {
+    const int so = static_cast<int>(k0 * 2);
+#pragma unroll
+    for (int j = 0; j < kCopyW; ++j) lds_copy16(wrs, wbuf + (wave_s * kCopyW + j) * 8 * kGemmBK, w_off[j], so);
+#pragma unroll
+    for (int j = 0; j < kCopyA; ++j) lds_copy16(xrs, abuf + (wave_s * kCopyA + j) * 8 * kGemmBK, a_off[j], so);
+  };
+
+  const int wc = wave / kGemmWavesT;  // feature slice of the block
+  const int wt = wave % kGemmWavesT;  // token slice of the block
+  f32x16 acc[kWaveBF][kWaveBT];
+#pragma unroll
+  for (int i = 0; i < kWaveBF; ++i)
+#pragma unroll
+    for (int j = 0; j < kWaveBT; ++j) acc[i][j] = f32x16{};
+
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const int swz = (l32 >> 1) & 7;  // rows of an MFMA block start at multiples of 32
+  auto multiply = [&](const uint16_t* wb, const uint16_t* ab) {
+#pragma unroll
+    for (int kk16 = 0; kk16 < kGemmBK / 16; ++kk16) {
+      const int pc = ((2 * kk16 + hi) ^ swz) * 8;  // physical chunk of logical chunk 2*kk16 + hi
+      bf16x8 fw[kWaveBF], ft[kWaveBT];
+#pragma unroll
+      for (int i = 0; i < kWaveBF; ++i)
+        fw[i] = *reinterpret_cast<const bf16x8*>(&wb[((wc * kWaveBF + i) * 32 + l32) * kGemmBK + pc]);
+#pragma unroll
+      for (int j = 0; j < kWaveBT; ++j)
+        ft[j] = *reinterpret_cast<const bf16x8*>(&ab[((wt * kWaveBT + j) * 32 + l32) * kGemmBK + pc]);
+#pragma unroll
+      for (int i = 0; i < kWaveBF; ++i)
+#pragma unroll
+        for (int j = 0; j < kWaveBT; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[i], ft[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  const long n_k = dim / kGemmBK;
+  copy_step(ws0, as0, 0);
+  lds_copy_wait();
+  __syncthreads();
+  long ks = 0;
+  for (; ks + 2 <= n_k; ks += 2) {
+    copy_step(ws1, as1, (ks + 1) * kGemmBK);
+    __builtin_amdgcn_sched_barrier(0);  // the copies go out before the MFMAs
+    multiply(ws0, as0);
+    lds_copy_wait();
+    __syncthreads();
+    if (ks + 2 < n_k) copy_step(ws0, as0, (ks + 2) * kGemmBK);
+    __builtin_amdgcn_sched_barrier(0);
+    multiply(ws1, as1);
+    lds_copy_wait();
+    __syncthreads();
+  }
+  if (ks < n_k) multiply(ws0, as0);  // odd step count: the last step was copied into buffer 0
+
+  store_tile<TL>(a, acc, c_base, t_base, wc, wt, lane);
 }
 
 template <typename TL>
@@ -321,6 +458,8 @@ void launch_tile(const GemmArgs& a, const RowSource& src, long n, hipStream_t s)
     hipLaunchKernelGGL((qkv_gemm_kernel<kSrcRecover, TL>), grid, dim3(TL::kThreads), 0, s, a);
   } else if (src.x_dtype == kDtypeF32) {
     hipLaunchKernelGGL((qkv_gemm_kernel<kSrcF32, TL>), grid, dim3(TL::kThreads), 0, s, a);
+  } else if (TL::kMinBlocks == 1) {
+    hipLaunchKernelGGL((qkv_gemm_lds_kernel<TL>), grid, dim3(TL::kThreads), 0, s, a);
   } else {
     hipLaunchKernelGGL((qkv_gemm_kernel<kSrcBf16, TL>), grid, dim3(TL::kThreads), 0, s, a);
   }
