@@ -444,6 +444,47 @@ def test_qkv_large_tile_sampled(src):
     assert not kc[others].any() and not vc[others].any()
 
 
+@pytest.mark.parametrize("kv_only,rope", [(False, None), (True, None), (False, (30, 40))])
+def test_qkv_lds_staging_equals_register_staging(kv_only, rope):
+    """Grids of at least 1024 256x256 tiles copy bf16 operands straight into LDS; a call on a
+    few of the same rows runs the register-staged 128x128 tile.  Both accumulate every output
+    in the same order (ascending 16-deep K chunks in fp32), so the rows agree bit for bit --
+    here with the ragged last token tile, K/V written into cache rows (features from D on),
+    and 3D rotary positions in the epilogue."""
+    t = tsa()
+    n_x, m, dim, heads = 12000, 11001, 3072, 24  # K/V only: 24 x 43 large tiles
+    g = torch.Generator().manual_seed(11)
+    x = G.dev(_randn_bf16(g, n_x, dim))
+    w = G.dev((torch.randn(3 * dim, dim, generator=g) / math.sqrt(dim)).to(torch.bfloat16))
+    rows = np.sort(np.random.default_rng(12).choice(n_x, m, replace=False)).astype(np.int32)
+    pick = np.unique(np.concatenate([np.arange(0, m, 997), np.arange(m - 40, m)]))
+    assert (3 * dim // 256) * ((m + 255) // 256) >= 1024 and (2 * dim // 256) * ((m + 255) // 256) >= 1024
+    assert (3 * dim // 256) * ((len(pick) + 255) // 256) < 1024
+
+    def run(r):
+        n = len(r)
+        rd = G.dev(torch.from_numpy(r))
+        if kv_only:
+            kc = torch.zeros(n_x, dim, dtype=torch.bfloat16, device="cuda")
+            vc = torch.zeros_like(kc)
+            t.qkv_active(x, rd, n, w, k_out=kc, v_out=vc, out_is_cache=True, n_cache=n_x)
+            rl = rd.long()
+            return [kc[rl], vc[rl]]
+        out = [torch.empty(n, dim, dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+        if rope is None:
+            t.qkv_active(x, rd, n, w, q_out=out[0], k_out=out[1], v_out=out[2])
+        else:
+            t.qkv_active_rope(x, rd, n, w, heads, rope[0], rope[1], q_out=out[0], k_out=out[1], v_out=out[2])
+        return out
+
+    full = run(rows)
+    few = run(rows[pick])
+    torch.cuda.synchronize()
+    pk = torch.from_numpy(pick).cuda()
+    for a, b in zip(full, few):
+        assert torch.equal(a[pk], b)
+
+
 @pytest.mark.parametrize("n_x,m,dim,rope", [(2000, 777, 1536, None), (9000, 7461, 3072, None),
                                             (1200, 500, 512, (6, 10, 4))])
 def test_rows_to_cache_equals_fused_recovery(n_x, m, dim, rope):
