@@ -445,12 +445,12 @@ def test_qkv_large_tile_sampled(src):
 
 
 @pytest.mark.parametrize("kv_only,rope", [(False, None), (True, None), (False, (30, 40))])
-def test_qkv_lds_staging_equals_register_staging(kv_only, rope):
-    """Grids of at least 1024 256x256 tiles copy bf16 operands straight into LDS; a call on a
-    few of the same rows runs the register-staged 128x128 tile.  Both accumulate every output
-    in the same order (ascending 16-deep K chunks in fp32), so the rows agree bit for bit --
-    here with the ragged last token tile, K/V written into cache rows (features from D on),
-    and 3D rotary positions in the epilogue."""
+def test_qkv_large_and_small_tiles_agree_bit_for_bit(kv_only, rope):
+    """Grids of at least 1024 256x256 tiles run the large tile; a call on a few of the same
+    rows runs the 128x128 tile.  Both accumulate every output in the same order (ascending
+    16-deep K chunks in fp32), so the rows agree bit for bit -- here with the ragged last
+    token tile, K/V written into cache rows (features from D on), and 3D rotary positions in
+    the epilogue."""
     t = tsa()
     n_x, m, dim, heads = 12000, 11001, 3072, 24  # K/V only: 24 x 43 large tiles
     g = torch.Generator().manual_seed(11)

@@ -22,11 +22,11 @@
 // 16-byte LDS reads feed eight MFMAs, and each staged K slice is shared by 256
 // columns and 256 tokens.  Two LDS buffers, one barrier per K step.  Grids of
 // fewer than four such tiles per CU use 128 x 128 tiles on 4 waves instead (two
-// workgroups per CU).  On the large tile, bf16 rows are copied from HBM straight
+// workgroups per CU).  bf16 rows -- the common case -- are copied from HBM straight
 // into LDS (qkv_gemm_lds_kernel: no registers, the next K step's copy in flight
-// while the current one is multiplied); otherwise, and for rows that need
-// arithmetic on the way (the recovery blend, fp32 input), operands go through
-// registers, loaded two K steps ahead (qkv_gemm_kernel).  All rows arrive through
+// while the current one is multiplied); rows that need arithmetic on the way (the
+// recovery blend, fp32 input) go through registers, loaded two K steps ahead
+// (qkv_gemm_kernel).  All rows arrive through
 // range-checked buffer loads (invalid rows read as zeros, no per-step selects).
 #include "common.h"
 #include "kernels.h"
@@ -195,11 +195,12 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, const f32x16 (&acc
   }
 }
 
-// Operand rows staged through registers, loaded two K steps ahead and stored to
-// padded LDS rows one step ahead (converted on the way for the recovery blend and
-// fp32 input).
+// Rows that need arithmetic on the way (the recovery blend, fp32 input): staged
+// through registers, loaded two K steps ahead and converted when stored to padded
+// LDS rows one step ahead.
 template <int SRC, typename TL>
 __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void qkv_gemm_kernel(GemmArgs a) {
+  static_assert(SRC == kSrcRecover || SRC == kSrcF32, "bf16 rows take qkv_gemm_lds_kernel");
   constexpr int kGemmBM = TL::kBM, kGemmBN = TL::kBN, kGemmWavesT = TL::kWavesT;
   constexpr int kWaveBF = TL::kBF, kWaveBT = TL::kBT;
   constexpr int kLoadRows = TL::kLoadRows, kLoadW = TL::kLoadW, kLoadA = TL::kLoadA;
@@ -221,7 +222,6 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void qkv_gemm_kernel(
       const_cast<void*>(a.x), 0, static_cast<int>(a.n_x_rows * dim * 2), kBufferRsrcFlags);
   // The A chunks are loaded raw and converted only when written to LDS, one K
   // step later, so the conversion never waits on a load just issued.
-  //   bf16:     raw[0] = the row chunk
   //   recovery: raw[0] = clean chunk (zeros when the token has no clean row), raw[1] = noise
   //   fp32:     raw[0], raw[1] = the two 16-byte halves (invalid rows read row 0, zeroed at the store)
   const __amdgpu_buffer_rsrc_t ers = __builtin_amdgcn_make_buffer_rsrc(
@@ -252,8 +252,7 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void qkv_gemm_kernel(
     }
   }
 
-  constexpr int kRaw = SRC == kSrcBf16 ? 1 : 2;
-  u32x4 wreg[kLoadW], araw[kLoadA][kRaw];
+  u32x4 wreg[kLoadW], araw[kLoadA][2];
   auto load_tiles = [&](long k0) {
     const int so = static_cast<int>(k0 * 2);
 #pragma unroll
@@ -267,15 +266,12 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void qkv_gemm_kernel(
         araw[j][1] = __builtin_bit_cast(u32x4, p[1]);
       } else {
         araw[j][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, x_off[j], so, 0));
-        if constexpr (SRC == kSrcRecover)
-          araw[j][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ers, e_off[j], so, 0));
+        araw[j][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ers, e_off[j], so, 0));
       }
     }
   };
   auto a_chunk = [&](int j) -> u32x4 {
-    if constexpr (SRC == kSrcBf16) {
-      return araw[j][0];
-    } else if constexpr (SRC == kSrcRecover) {
+    if constexpr (SRC == kSrcRecover) {
       return recover8(araw[j][0], araw[j][1], 1.0f - a.sigma, a.sigma);
     } else {
       const f32x4 lo = __builtin_bit_cast(f32x4, araw[j][0]), hi = __builtin_bit_cast(f32x4, araw[j][1]);
@@ -458,10 +454,8 @@ void launch_tile(const GemmArgs& a, const RowSource& src, long n, hipStream_t s)
     hipLaunchKernelGGL((qkv_gemm_kernel<kSrcRecover, TL>), grid, dim3(TL::kThreads), 0, s, a);
   } else if (src.x_dtype == kDtypeF32) {
     hipLaunchKernelGGL((qkv_gemm_kernel<kSrcF32, TL>), grid, dim3(TL::kThreads), 0, s, a);
-  } else if (TL::kMinBlocks == 1) {
-    hipLaunchKernelGGL((qkv_gemm_lds_kernel<TL>), grid, dim3(TL::kThreads), 0, s, a);
   } else {
-    hipLaunchKernelGGL((qkv_gemm_kernel<kSrcBf16, TL>), grid, dim3(TL::kThreads), 0, s, a);
+    hipLaunchKernelGGL((qkv_gemm_lds_kernel<TL>), grid, dim3(TL::kThreads), 0, s, a);
   }
 }
 
