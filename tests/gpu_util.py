@@ -54,7 +54,10 @@ def assert_close(got, want, what="", rel=REL_FROB, mabs=MAX_ABS):
     want = np.asarray(want, np.float64)
     rf, ma = rel_frob(got, want), max_abs(got, want)
     sc = float(np.max(np.abs(got - want) / np.maximum(1.0, np.abs(want)))) if got.size else 0.0
-    print(f"  {what}: rel_frob={rf:.3e} max_abs={ma:.3e} scaled_max_abs={sc:.3e}", flush=True)
+    # elements whose unscaled error exceeds the fixed 2e-2 (those sit where |want| > 1)
+    n_over = int(np.count_nonzero(np.abs(got - want) > MAX_ABS))
+    print(f"  {what}: rel_frob={rf:.3e} max_abs={ma:.3e} scaled_max_abs={sc:.3e} "
+          f"above_{MAX_ABS:g}={n_over} of {got.size}", flush=True)
     assert rf <= rel and sc <= mabs, f"{what}: rel_frob={rf:.3e} max_abs={ma:.3e} scaled={sc:.3e}"
 
 

@@ -154,6 +154,33 @@ def test_concurrent_streams_match_sequential_steps():
             assert torch.equal(x, y)
 
 
+def test_threshold_step_on_a_side_stream_reads_its_own_count():
+    """step_threshold on a stream other than the current one: the active count is read back
+    after the selection queued on that stream (which starts late behind a long product), so
+    the step uses the count of this selection, not whatever the buffer held."""
+    t = tsa()
+    cfg = scaled(configs.get_config("wan13b"), frames=2, height=20, width=52)
+    inp = generate.step_inputs(cfg, 3)
+    xp64, xc64 = G.host64(inp["x_prev"]), G.host64(inp["x_cur"])
+    tau = 0.1  # between the static (about 0.01) and the moving (about 0.5) scores
+    want = ref.select_threshold(ref.token_scores(xc64, xp64), tau)
+    layer = t.PrunedAttentionLayer(cfg.n, cfg.dim, cfg.heads, G.dev(inp["w_qkv"]))
+    xp, xc = G.dev(inp["x_prev"]), G.dev(inp["x_cur"])
+    layer.init_cache(xp)
+    layer.n_active.fill_(-5)
+    big = torch.randn(4096, 4096, device="cuda")
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        for _ in range(8):
+            big = big @ big.T / 64.0  # keeps the side stream busy before the selection
+    n_act = layer.step_threshold(xc, xp, tau, stream=side)
+    torch.cuda.synchronize()
+    assert n_act == int(want.sum())
+    idx, _ = ref.compact(want)
+    assert np.array_equal(layer.idx.cpu().numpy()[:n_act], idx)
+
+
 def test_threshold_step_zero_change_leaves_state():
     t = tsa()
     cfg = scaled(configs.get_config("wan13b"), frames=2, height=10, width=16)
@@ -270,6 +297,8 @@ def _lipar_case(cfg, pct_index, seed=0, sample=None):
     d = cfg.dim
     G.assert_projection_close(gk[sm], kc[sm], ax @ np.abs(w64[d:2 * d]).T, d, "K cache (active rows)")
     G.assert_projection_close(gv[sm], vc[sm], ax @ np.abs(w64[2 * d:]).T, d, "V cache (active rows)")
+    G.assert_close(gk[idx], kc[idx], "K cache (all active rows)", mabs=np.inf)
+    G.assert_close(gv[idx], vc[idx], "V cache (all active rows)", mabs=np.inf)
     if pidx.size:
         # rows from recovered inputs: those inputs carry their own fp32 rounding, so compare
         # with the layer tolerance, max-abs taken relative to max(1, |value|)
@@ -305,5 +334,68 @@ def test_large_full_size_sampled():
 
 
 @pytest.mark.slow
-def test_lipar_full_size_sampled():
-    _lipar_case(configs.get_config("lipar"), 2, sample=48)
+@pytest.mark.parametrize("pct_index", [0, 1, 2, 3, 4])
+def test_lipar_full_size_sampled(pct_index):
+    """LIPAR sweep at full size (N = 118800, D = 3072, 24 heads): 5 / 10 / 25 / 50 / 100 %
+    active; 100 % is the dense check (every row projected from its own latent)."""
+    _lipar_case(configs.get_config("lipar"), pct_index, sample=48)
+
+
+@pytest.mark.slow
+def test_hsa_schedule_full_size_every_step():
+    """The HSA 8-step schedule at full size (N = 32760, D = 1536, 12 heads; per-step active
+    counts N, N/4, N/2, N/4, N, N/4, N/2, N/4): the period of every token and the whole active
+    list of every step bit for bit; the whole K/V cache after every step against the oracle's
+    (fresh rows within the projection bound on a sample, stale rows bit-identical to the
+    previous step); a seeded sample of the step's output rows against the oracle's attention
+    over its own cache; output rows of skipped tokens bit-identical to the previous step."""
+    t = tsa()
+    cfg = configs.get_config("hsa")
+    print(f"  case {cfg.name} N={cfg.n} D={cfg.dim} H={cfg.heads} T={cfg.steps}", flush=True)
+    inp = generate.hsa_inputs(cfg, 0)
+    xs, w = inp["xs"], inp["w_qkv"]
+    counts, periods = cfg.group_counts(), cfg.group_periods()
+    d = cfg.dim
+    layer = t.PrunedAttentionLayer(cfg.n, cfg.dim, cfg.heads, G.dev(w))
+    layer.init_cache(G.dev(xs[0]))
+    layer.select(G.dev(xs[1]), G.dev(xs[0]), k=1)
+    period = torch.empty(cfg.n, dtype=torch.uint8, device="cuda")
+    t.assign_groups(layer.scores, counts, periods, period, layer.workspace)
+    torch.cuda.synchronize()
+
+    w64 = G.host64(w)
+    wk, wv = np.abs(w64[d:2 * d]), np.abs(w64[2 * d:])
+    kc, vc = ref.init_kv_cache(G.host64(xs[0]), w64)
+    per = ref.assign_periods(ref.token_scores(G.host64(xs[1]), G.host64(xs[0])), counts, periods)
+    assert np.array_equal(period.cpu().numpy(), per)
+    prev_k, prev_v = G.host64(layer.k_cache), G.host64(layer.v_cache)
+    prev_out = G.host64(layer.out)
+    rng = np.random.default_rng(17)
+    for i in range(cfg.steps):
+        n_act = t.hsa_active_count(counts, periods, i)
+        layer.select(None, periods=period, step=i)
+        layer.forward_active(G.dev(xs[i + 1]), n_act)
+        torch.cuda.synchronize()
+        mask = ref.schedule_mask(per, i)
+        idx, pidx = ref.compact(mask)
+        print(f"  step {i}: {idx.size} active", flush=True)
+        assert idx.size == n_act
+        assert np.array_equal(layer.idx.cpu().numpy()[:n_act], idx)
+        assert np.array_equal(layer.pidx.cpu().numpy()[:pidx.size], pidx)
+        assert int(layer.n_active.item()) == n_act
+        x64 = G.host64(xs[i + 1])
+        p = ref.project(x64[idx], w64, "kv")
+        ref.kv_cache_sync(kc, vc, idx, p["k"], p["v"])
+        gk, gv, go = G.host64(layer.k_cache), G.host64(layer.v_cache), G.host64(layer.out)
+        G.assert_close(gk, kc, f"step {i} K cache (all rows)", mabs=np.inf)
+        G.assert_close(gv, vc, f"step {i} V cache (all rows)", mabs=np.inf)
+        fr = idx if idx.size <= 8192 else np.sort(rng.choice(idx, 8192, replace=False))
+        ax = np.abs(ref.round_bf16(x64[fr]))
+        G.assert_projection_close(gk[fr], kc[fr], ax @ wk.T, d, f"step {i} K cache (fresh rows)")
+        G.assert_projection_close(gv[fr], vc[fr], ax @ wv.T, d, f"step {i} V cache (fresh rows)")
+        assert np.array_equal(gk[pidx], prev_k[pidx]) and np.array_equal(gv[pidx], prev_v[pidx])
+        assert np.array_equal(go[pidx], prev_out[pidx])  # skipped tokens keep their output
+        rows = np.sort(rng.choice(idx.size, 48, replace=False))
+        q = ref.project(x64[idx[rows]], w64, "q")["q"]
+        G.assert_close(go[idx[rows]], ref.attention(q, kc, vc, cfg.heads), f"step {i} sampled output rows")
+        prev_k, prev_v, prev_out = gk, gv, go

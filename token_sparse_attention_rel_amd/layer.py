@@ -52,9 +52,11 @@ class PrunedAttentionLayer:
         # partials of the attention's split last round, grown on demand
         self.split_attention = split_attention
         self._attn_ws = torch.empty(0, dtype=torch.uint8, device=dev)
+        self._attn_ws_streams = []  # streams other than the allocating one that used it
 
-    def attention_workspace(self, n_q: int):
-        """Workspace for attention of n_q active queries over the cache (None: no split)."""
+    def attention_workspace(self, n_q: int, stream=None):
+        """Workspace for attention of n_q active queries over the cache (None: no split),
+        to be used on ``stream`` (None: the current stream)."""
         if not self.split_attention:
             return None
         with torch.cuda.device(self.device):
@@ -62,7 +64,14 @@ class PrunedAttentionLayer:
         if need == 0:
             return None
         if self._attn_ws.numel() < need:
+            # the old buffer may still be read by work queued on another stream: the
+            # allocator must not hand it out again before that work is done
+            for st in self._attn_ws_streams:
+                self._attn_ws.record_stream(st)
             self._attn_ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+            self._attn_ws_streams = []
+        if stream is not None and stream not in self._attn_ws_streams:
+            self._attn_ws_streams.append(stream)
         return self._attn_ws
 
     # ---------------------------------------------------------------- state
@@ -78,7 +87,7 @@ class PrunedAttentionLayer:
         """Attention of the n_q queries in q_a (tokens q_tokens) over the cache."""
         if self.causal_frame_tokens is None:
             B.sparse_query_attention(self.q_a, self.k_cache, self.v_cache, n_q, self.heads, self.head_dim,
-                                     out, out_rows=rows, workspace=self.attention_workspace(n_q),
+                                     out, out_rows=rows, workspace=self.attention_workspace(n_q, stream),
                                      stream=stream)
         else:
             B.frame_causal_attention(self.q_a, self.k_cache, self.v_cache, n_q, self.heads, self.head_dim,
@@ -136,6 +145,14 @@ class PrunedAttentionLayer:
             self._attend(n_active, o_a, idx, stream=stream)
             B.scatter_out(o_a, idx, n_active, self.out, stream=stream)
 
+    def _read_n_active(self, stream=None) -> int:
+        """The active count of the last selection, read back after the selection queued on
+        ``stream`` (None: the current stream) has finished: the copy runs on that stream."""
+        if stream is None:
+            return int(self.n_active.item())
+        with torch.cuda.stream(stream):
+            return int(self.n_active.item())
+
     def step_topk(self, x_cur, x_ref, k: int, *, fused=True, stream=None) -> None:
         """One step with a fixed active count k (no host synchronisation)."""
         self.select(x_cur, x_ref, k=k, stream=stream)
@@ -144,7 +161,7 @@ class PrunedAttentionLayer:
     def step_threshold(self, x_cur, x_ref, tau: float, *, fused=True, stream=None) -> int:
         """One step with s >= tau active; reads the active count back (one synchronisation)."""
         self.select(x_cur, x_ref, tau=tau, stream=stream)
-        n_active = int(self.n_active.item())
+        n_active = self._read_n_active(stream)
         self.forward_active(x_cur, n_active, fused=fused, stream=stream)
         return n_active
 
@@ -167,7 +184,7 @@ class PrunedAttentionLayer:
         B.lif_mask(x, frames, hw, tau_short, tau_long, self._lif_mask, score_kind=score_kind,
                    stream=stream)
         self.select(None, mask=self._lif_mask, stream=stream)
-        k = int(self.n_active.item())
+        k = self._read_n_active(stream)
         self._lipar_forward(x, eps, hw, k, sigma, stream)
         if restore:
             B.restore_frames(self.out, self._lif_mask, frames, hw, stream=stream)
@@ -211,7 +228,7 @@ class PrunedAttentionLayer:
         B.timeripple_reuse(self.k_cache, self.heads, self.head_dim, h, w, thetas_k, self._k_eff, self._reuse_ws,
                            src_out=self.src_k, stream=stream)
         B.sparse_query_attention(self._q_eff, self._k_eff, self.v_cache, self.n, self.heads, self.head_dim,
-                                 self.out, workspace=self.attention_workspace(self.n), stream=stream)
+                                 self.out, workspace=self.attention_workspace(self.n, stream), stream=stream)
 
     # ------------------------------------------------------- sampling loop
 
