@@ -405,6 +405,25 @@ tsa_status tsa_timeripple_reuse(const tsa_bf16* v, int64_t n_rows, int heads, in
                                 int64_t width, const float* thetas, tsa_bf16* v_eff, int32_t* src_out,
                                 float* delta_out, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * tsa_timeripple_reuse without a workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  The source and root tables live in a static device
+ * array of the library (24 MiB on each GPU it runs on, held until the process
+ * ends), so n_rows * heads may be at most tsa_reuse_noalloc_max_token_heads()
+ * (2^20).  Every call on one GPU uses that GPU's single array: calls that overlap
+ * on one GPU (several streams or host threads) race and must be ordered by the
+ * caller.  Nothing is allocated and no allocating routine is called.  Arguments,
+ * results and errors as tsa_timeripple_reuse; SHAPE also when n_rows * heads is
+ * above the maximum.
+ */
+tsa_status tsa_timeripple_reuse_noalloc(const tsa_bf16* v, int64_t n_rows, int heads, int head_dim, int64_t height,
+                                        int64_t width, const float* thetas, tsa_bf16* v_eff, int32_t* src_out,
+                                        float* delta_out, void* stream);
+
+/* Largest n_rows * heads tsa_timeripple_reuse_noalloc accepts (2^20). */
+size_t tsa_reuse_noalloc_max_token_heads(void);
+
 #ifdef __cplusplus
 }
 #endif

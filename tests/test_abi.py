@@ -235,6 +235,23 @@ def test_reuse_validation():
     assert ru(ws=None) == B.ERR_WORKSPACE
     assert ru(wsb=100) == B.ERR_WORKSPACE
 
+    # the variant without a workspace: the same checks, and at most 2^20 token-heads
+    def rn(th=(0.1, 0.1, 0.1), **kw):
+        t = (ctypes.c_float * 3)(*th)
+        a = dict(v=A, n=64, heads=2, hd=128, h=4, w=4, eff=A + big, src=None, delta=None)
+        a.update(kw)
+        return f.tsa_timeripple_reuse_noalloc(a["v"], a["n"], a["heads"], a["hd"], a["h"], a["w"],
+                                              ctypes.cast(t, ctypes.c_void_p), a["eff"], a["src"], a["delta"],
+                                              None)
+    assert tsa.reuse_noalloc_max_token_heads() == 1 << 20
+    assert rn(n=0) == B.OK
+    assert rn(v=None) == B.ERR_INVALID_ARG
+    assert rn(th=(0.1, float("nan"), 0.1)) == B.ERR_INVALID_ARG
+    assert rn(eff=A + 64) == B.ERR_INVALID_ARG
+    assert rn(hd=96) == B.ERR_SHAPE
+    assert rn(v=U) == B.ERR_ALIGNMENT
+    assert rn(n=(1 << 19) + 1, heads=2) == B.ERR_SHAPE  # above 2^20 token-heads
+
 
 def test_qkv_rows_to_cache_validation():
     f = lib()

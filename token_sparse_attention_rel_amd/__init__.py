@@ -42,7 +42,9 @@ from ._binding import (
     select_workspace_bytes,
     sparse_query_attention,
     status_string,
+    reuse_noalloc_max_token_heads,
     timeripple_reuse,
+    timeripple_reuse_noalloc,
     token_scores,
 )
 from .layer import PrunedAttentionLayer, hsa_active_count
@@ -54,5 +56,6 @@ __all__ = [
     "SELECT_THRESHOLD", "SELECT_TOPK", "TsaError", "abi_version", "assign_groups", "attention_workspace_bytes", "euler_update", "frame_causal_attention", "gather_rows",
     "kv_cache_sync", "lib", "lib_path", "lif_mask", "qkv_active", "qkv_active_rope", "restore_frames", "scatter_out", "select_active",
     "select_workspace_bytes", "sparse_query_attention", "status_string", "token_scores",
+    "timeripple_reuse", "timeripple_reuse_noalloc", "reuse_noalloc_max_token_heads",
     "PrunedAttentionLayer", "hsa_active_count",
 ]

@@ -55,6 +55,8 @@ _SIGNATURES = {
     "tsa_reuse_workspace_bytes": (_size, [_i64, _int]),
     "tsa_qkv_rows_to_cache": (_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _int, _i64, _i64, _f32, _vp]),
     "tsa_timeripple_reuse": (_int, [_vp, _i64, _int, _int, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _size, _vp]),
+    "tsa_timeripple_reuse_noalloc": (_int, [_vp, _i64, _int, _int, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
+    "tsa_reuse_noalloc_max_token_heads": (_size, []),
 }
 
 _lib_handle = None
@@ -371,6 +373,28 @@ def timeripple_reuse(v, heads, head_dim, height, width, thetas, eff_out, workspa
                                     0 if workspace is None else workspace.numel() * workspace.element_size(),
                                     _stream(stream))
     _check("tsa_timeripple_reuse", st)
+
+
+def timeripple_reuse_noalloc(v, heads, head_dim, height, width, thetas, eff_out, *, src_out=None,
+                             delta_out=None, stream=None):
+    """tsa_timeripple_reuse with the library's static scratch instead of a workspace
+    (tsa_timeripple_reuse_noalloc): for callers that cannot allocate device memory."""
+    dim = int(heads) * int(head_dim)
+    n = v.shape[0]
+    _need(v, "v", ("bf16",), cols=dim)
+    _need(eff_out, "eff_out", ("bf16",), rows=n, cols=dim)
+    _need(src_out, "src_out", ("i32",), numel=n * int(heads) * 3)
+    _need(delta_out, "delta_out", ("f32",), numel=n * int(heads) * 3)
+    th = (ctypes.c_float * 3)(*[float(t) for t in thetas])
+    st = lib().tsa_timeripple_reuse_noalloc(_ptr(v), int(v.shape[0]), int(heads), int(head_dim), int(height),
+                                            int(width), ctypes.cast(th, ctypes.c_void_p), _ptr(eff_out),
+                                            _ptr(src_out), _ptr(delta_out), _stream(stream))
+    _check("tsa_timeripple_reuse_noalloc", st)
+
+
+def reuse_noalloc_max_token_heads() -> int:
+    """Largest n_rows * heads timeripple_reuse_noalloc accepts."""
+    return int(lib().tsa_reuse_noalloc_max_token_heads())
 
 
 def token_scores(x_cur, x_ref, scores_out, *, ref_row_offset=0, score_kind=SCORE_REL_L1, stream=None):

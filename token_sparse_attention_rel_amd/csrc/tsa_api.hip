@@ -6,6 +6,8 @@
 // the attention kernel's resident workgroup count.
 #include <math.h>
 
+#include <mutex>
+
 #include "../../include/tsa.h"
 #include "kernels.h"
 
@@ -361,9 +363,13 @@ size_t tsa_reuse_workspace_bytes(int64_t n_rows, int heads) {
   return static_cast<size_t>(2) * static_cast<size_t>(n_rows) * static_cast<size_t>(heads) * 3 * 4;
 }
 
-tsa_status tsa_timeripple_reuse(const tsa_bf16* v, int64_t n_rows, int heads, int head_dim, int64_t height,
-                                int64_t width, const float* thetas, tsa_bf16* v_eff, int32_t* src_out,
-                                float* delta_out, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of tsa_timeripple_reuse (everything but the workspace).
+tsa_status check_reuse(const tsa_bf16* v, int64_t n_rows, int heads, int head_dim, int64_t height, int64_t width,
+                       const float* thetas, const tsa_bf16* v_eff, const int32_t* src_out, const float* delta_out) {
   if (!v || !v_eff || !thetas) return TSA_ERR_INVALID_ARG;
   for (int a = 0; a < 3; ++a)
     if (isnan(thetas[a]) || thetas[a] < 0.f) return TSA_ERR_INVALID_ARG;
@@ -379,10 +385,66 @@ tsa_status tsa_timeripple_reuse(const tsa_bf16* v, int64_t n_rows, int heads, in
   if (n_rows > 0 && vb < eb + span && eb < vb + span) return TSA_ERR_INVALID_ARG;  // overlap
   if (!aligned16(v) || !aligned16(v_eff) || (src_out && !aligned4(src_out)) || (delta_out && !aligned4(delta_out)))
     return TSA_ERR_ALIGNMENT;
+  return TSA_OK;
+}
+
+// Scratch of tsa_timeripple_reuse_noalloc: the source and root tables (n * heads * 3
+// int32 each) for up to kNoallocMaxTokenHeads token-heads.  One copy per GPU, held
+// until the process ends; every entry a call reads is written earlier in the same call,
+// so nothing has to start at zero.
+constexpr int64_t kNoallocMaxTokenHeads = int64_t{1} << 20;
+constexpr size_t kNoallocScratchBytes = 2 * 3 * 4 * static_cast<size_t>(kNoallocMaxTokenHeads);  // 24 MiB
+__device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+constexpr int kNoallocMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kNoallocMaxDevices];  // device address of `scratch` on each device, once looked up
+
+// The device address of `scratch` on the current device (looked up the first time the
+// device is seen, with that device current).
+tsa_status noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kNoallocMaxDevices) return TSA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return TSA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return TSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tsa_status tsa_timeripple_reuse(const tsa_bf16* v, int64_t n_rows, int heads, int head_dim, int64_t height,
+                                int64_t width, const float* thetas, tsa_bf16* v_eff, int32_t* src_out,
+                                float* delta_out, void* workspace, size_t workspace_bytes, void* stream) {
+  const tsa_status st = check_reuse(v, n_rows, heads, head_dim, height, width, thetas, v_eff, src_out, delta_out);
+  if (st != TSA_OK) return st;
   if (n_rows == 0) return TSA_OK;
   if (!workspace || workspace_bytes < tsa_reuse_workspace_bytes(n_rows, heads)) return TSA_ERR_WORKSPACE;
   if (!aligned4(workspace)) return TSA_ERR_ALIGNMENT;
   int* ws_src = static_cast<int*>(workspace);
+  int* ws_root = ws_src + n_rows * heads * 3;
+  return from_hip(tsa::launch_reuse(v, n_rows, heads, head_dim, height, width, thetas, v_eff, src_out, delta_out,
+                                    ws_src, ws_root, as_stream(stream)));
+}
+
+size_t tsa_reuse_noalloc_max_token_heads(void) { return static_cast<size_t>(kNoallocMaxTokenHeads); }
+
+tsa_status tsa_timeripple_reuse_noalloc(const tsa_bf16* v, int64_t n_rows, int heads, int head_dim, int64_t height,
+                                        int64_t width, const float* thetas, tsa_bf16* v_eff, int32_t* src_out,
+                                        float* delta_out, void* stream) {
+  const tsa_status st = check_reuse(v, n_rows, heads, head_dim, height, width, thetas, v_eff, src_out, delta_out);
+  if (st != TSA_OK) return st;
+  if (n_rows * heads > kNoallocMaxTokenHeads) return TSA_ERR_SHAPE;
+  if (n_rows == 0) return TSA_OK;
+  void* ws = nullptr;
+  const tsa_status sst = noalloc_scratch(&ws);
+  if (sst != TSA_OK) return sst;
+  int* ws_src = static_cast<int*>(ws);
   int* ws_root = ws_src + n_rows * heads * 3;
   return from_hip(tsa::launch_reuse(v, n_rows, heads, head_dim, height, width, thetas, v_eff, src_out, delta_out,
                                     ws_src, ws_root, as_stream(stream)));
