@@ -27,7 +27,11 @@
  *     is dimension j of head h.  bf16 values are passed as raw 16-bit words
  *     (tsa_bf16).  Row buffers must be 16-byte aligned.
  *   - Index lists are int32, ascending, without repeats, within range.  This
- *     is a precondition (the kernels clamp nothing and do not check it).
+ *     is a precondition: the release build's kernels clamp nothing and do not
+ *     check it.  The debug build (libtsa_debug.so, compiled with TSA_DEBUG)
+ *     checks every index list on the GPU before a kernel reads it and returns
+ *     TSA_ERR_SHAPE for a violation (synchronising the stream to do so);
+ *     query-token lists are only checked to be non-negative.
  *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only
  *     enqueues work on it and returns; nothing synchronises.  Device faults
  *     surface at the caller's next synchronisation.

@@ -248,6 +248,30 @@ def test_hsa_schedule_loop_scaled():
                                   ax @ np.abs(w64[cfg.dim:2 * cfg.dim]).T, cfg.dim, f"step {i} fresh K")
 
 
+def test_debug_layer_checks_the_host_count():
+    """With debug=True a step given the wrong active count raises before any kernel runs
+    with it; the right count runs as usual."""
+    t = tsa()
+    cfg = scaled(configs.get_config("hsa"), frames=2, height=6, width=20)
+    inp = generate.hsa_inputs(cfg, 0)
+    layer = t.PrunedAttentionLayer(cfg.n, cfg.dim, cfg.heads, G.dev(inp["w_qkv"]), debug=True)
+    xs = [G.dev(x) for x in inp["xs"]]
+    layer.init_cache(xs[0])
+    layer.select(xs[1], xs[0], k=1)
+    counts, periods = cfg.group_counts(), cfg.group_periods()
+    period = torch.empty(cfg.n, dtype=torch.uint8, device="cuda")
+    t.assign_groups(layer.scores, counts, periods, period, layer.workspace)
+    layer.select(None, periods=period, step=1)
+    right = t.hsa_active_count(counts, periods, 1)
+    out0 = layer.out.clone()
+    with pytest.raises(ValueError):
+        layer.forward_active(xs[2], right + 1)
+    torch.cuda.synchronize()
+    assert torch.equal(layer.out, out0)
+    layer.forward_active(xs[2], right)
+    torch.cuda.synchronize()
+
+
 def _lipar_case(cfg, pct_index, seed=0, sample=None):
     t = tsa()
     inp = generate.lipar_inputs(cfg, seed)

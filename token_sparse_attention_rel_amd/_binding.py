@@ -14,7 +14,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtsa.so")
+# The in-tree build; TSA_LIB names another build of the same library (the debug build with
+# index-list checks, or a sanitizer build of the host code).
+_LIB_PATH = os.environ.get("TSA_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtsa.so")
 
 # Values of the C enums (include/tsa.h).
 OK = 0

@@ -26,6 +26,46 @@ tsa_status from_hip(hipError_t e) { return e == hipSuccess ? TSA_OK : TSA_ERR_HI
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
+#ifdef TSA_DEBUG
+// Debug builds check the documented preconditions of every index list before any
+// kernel reads it: entries in [0, limit) and, for token lists, strictly increasing.
+// A violation comes back as TSA_ERR_SHAPE (the check synchronises the stream);
+// release builds skip it.
+__device__ int debug_violation;
+
+__global__ void debug_reset_kernel(int* flag) { *flag = 0; }
+
+__global__ void debug_rows_kernel(const int32_t* rows, long n, long limit, int increasing, int* flag) {
+  for (long i = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<long>(gridDim.x) * blockDim.x) {
+    const long r = rows[i];
+    if (r < 0 || r >= limit || (increasing && i > 0 && static_cast<long>(rows[i - 1]) >= r)) *flag = 1;
+  }
+}
+
+bool debug_rows_ok(const int32_t* rows, int64_t n, int64_t limit, bool increasing, hipStream_t s) {
+  int* flag = nullptr;
+  if (hipGetSymbolAddress(reinterpret_cast<void**>(&flag), HIP_SYMBOL(debug_violation)) != hipSuccess) return false;
+  hipLaunchKernelGGL(debug_reset_kernel, dim3(1), dim3(1), 0, s, flag);
+  const long blocks = n / 256 + 1 < 1024 ? n / 256 + 1 : 1024;
+  hipLaunchKernelGGL(debug_rows_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, rows,
+                     static_cast<long>(n), static_cast<long>(limit), increasing ? 1 : 0, flag);
+  int h = 1;
+  if (hipMemcpyAsync(&h, flag, sizeof(int), hipMemcpyDeviceToHost, s) != hipSuccess) return false;
+  if (hipStreamSynchronize(s) != hipSuccess) return false;
+  return h == 0;
+}
+#define TSA_CHECK_ROWS(rows, n, limit, increasing, stream)                                  \
+  do {                                                                                      \
+    if ((rows) && !debug_rows_ok((rows), (n), (limit), (increasing), as_stream(stream))) \
+      return TSA_ERR_SHAPE;                                                                 \
+  } while (0)
+#else
+#define TSA_CHECK_ROWS(rows, n, limit, increasing, stream) \
+  do {                                                     \
+  } while (0)
+#endif
+
 }  // namespace
 
 extern "C" {
@@ -158,6 +198,7 @@ tsa_status tsa_qkv_active(const void* x, int x_dtype, int64_t n_x_rows, const in
       !aligned16(v_out) || (eps && !aligned16(eps)) || (rows && !aligned4(rows)))
     return TSA_ERR_ALIGNMENT;
   if (n == 0) return TSA_OK;
+  TSA_CHECK_ROWS(rows, n, out_is_cache && n_cache < n_x_rows ? n_cache : n_x_rows, true, stream);
   RowSource src{x, x_dtype, n_x_rows, rows, eps, src_row_offset, sigma};
   tsa::QkvOut out{q_out, k_out, v_out, out_is_cache ? 1 : 0};
   return from_hip(tsa::launch_qkv(src, n, dim, w_qkv, out, tsa::RopeSpec{}, as_stream(stream)));
@@ -188,6 +229,7 @@ tsa_status tsa_qkv_active_rope(const void* x, int x_dtype, int64_t n_x_rows, con
       !aligned16(v_out) || (eps && !aligned16(eps)) || (rows && !aligned4(rows)))
     return TSA_ERR_ALIGNMENT;
   if (n == 0) return TSA_OK;
+  TSA_CHECK_ROWS(rows, n, out_is_cache && n_cache < n_x_rows ? n_cache : n_x_rows, true, stream);
   RowSource src{x, x_dtype, n_x_rows, rows, eps, src_row_offset, sigma};
   tsa::QkvOut out{q_out, k_out, v_out, out_is_cache ? 1 : 0};
   tsa::RopeSpec rope;
@@ -222,6 +264,7 @@ tsa_status tsa_qkv_rows_to_cache(const tsa_bf16* a, int64_t n, int64_t dim, cons
       !aligned16(v_cache) || !aligned4(rows))
     return TSA_ERR_ALIGNMENT;
   if (n == 0) return TSA_OK;
+  TSA_CHECK_ROWS(rows, n, n_cache, true, stream);
   RowSource src{a, TSA_BF16, n, nullptr, nullptr, 0, 0.f};
   tsa::QkvOut out{q_out, k_cache, v_cache, 1, rows};
   return from_hip(tsa::launch_qkv(src, n, dim, w_qkv, out, rope, as_stream(stream)));
@@ -237,6 +280,7 @@ tsa_status tsa_kv_cache_sync(const tsa_bf16* k_a, const tsa_bf16* v_a, const int
       !aligned4(rows))
     return TSA_ERR_ALIGNMENT;
   if (n == 0) return TSA_OK;
+  TSA_CHECK_ROWS(rows, n, n_cache, true, stream);
   return from_hip(tsa::launch_copy_rows2(k_a, v_a, rows, n, k_cache, v_cache, dim,
                                          as_stream(stream)));
 }
@@ -260,6 +304,7 @@ tsa_status tsa_sparse_query_attention(const tsa_bf16* q, const tsa_bf16* k_cache
   if (n_q == 0) return TSA_OK;
   if (workspace && workspace_bytes < tsa::attention_workspace_bytes(n_q, n_kv, heads, head_dim))
     return TSA_ERR_WORKSPACE;
+  TSA_CHECK_ROWS(out_rows, n_q, n_out, true, stream);
   const float sc = scale > 0.f ? scale : 1.0f / sqrtf(static_cast<float>(head_dim));
   return from_hip(tsa::launch_attention(q, k_cache, v_cache, n_q, n_kv, heads, head_dim, sc, out,
                                         out_rows, lse_out, workspace, workspace_bytes,
@@ -282,6 +327,8 @@ tsa_status tsa_frame_causal_attention(const tsa_bf16* q, const tsa_bf16* k_cache
       (out_rows && !aligned4(out_rows)) || (lse_out && !aligned4(lse_out)))
     return TSA_ERR_ALIGNMENT;
   if (n_q == 0) return TSA_OK;
+  TSA_CHECK_ROWS(q_tokens, n_q, kMaxRows, false, stream);
+  TSA_CHECK_ROWS(out_rows, n_q, n_out, true, stream);
   const float sc = scale > 0.f ? scale : 1.0f / sqrtf(static_cast<float>(head_dim));
   return from_hip(tsa::launch_attention_causal(q, k_cache, v_cache, n_q, n_kv, heads, head_dim, sc, q_tokens,
                                                frame_tokens, out, out_rows, lse_out, as_stream(stream)));
@@ -301,6 +348,7 @@ tsa_status tsa_scatter_out(const tsa_bf16* o_a, const int32_t* rows, int64_t n, 
   if (n > n_out || dim <= 0 || dim % 8 != 0) return TSA_ERR_SHAPE;
   if (!aligned16(o_a) || !aligned16(out) || !aligned4(rows)) return TSA_ERR_ALIGNMENT;
   if (n == 0) return TSA_OK;
+  TSA_CHECK_ROWS(rows, n, n_out, true, stream);
   return from_hip(
       tsa::launch_copy_rows2(o_a, nullptr, rows, n, out, nullptr, dim, as_stream(stream)));
 }
@@ -315,6 +363,7 @@ tsa_status tsa_gather_rows(const tsa_bf16* x, int64_t n_x_rows, const int32_t* r
   if (!aligned16(x) || !aligned16(dst) || (eps && !aligned16(eps)) || !aligned4(rows))
     return TSA_ERR_ALIGNMENT;
   if (n == 0) return TSA_OK;
+  TSA_CHECK_ROWS(rows, n, n_x_rows, true, stream);
   RowSource src{x, TSA_BF16, n_x_rows, rows, eps, src_row_offset, sigma};
   return from_hip(tsa::launch_gather_rows(src, n, dim, dst, as_stream(stream)));
 }

@@ -18,14 +18,17 @@ from . import _binding as B
 
 class PrunedAttentionLayer:
     def __init__(self, n: int, dim: int, heads: int, w_qkv: torch.Tensor, device="cuda", *,
-                 split_attention: bool = True, rope=None, causal_frame_tokens=None):
+                 split_attention: bool = True, rope=None, causal_frame_tokens=None, debug: bool = False):
         """``rope = (height, width, base)`` rotates Q and K by their tokens' 3D positions
         (the cache then holds rotated K); ``causal_frame_tokens`` makes the attention
-        frame-causal (a query sees the frames up to its own)."""
+        frame-causal (a query sees the frames up to its own).  ``debug``: every
+        forward_active first reads the selection's active count back (one synchronisation)
+        and raises if the count it was given differs."""
         if dim % heads:
             raise ValueError("dim must be a multiple of heads")
         self.rope = rope
         self.causal_frame_tokens = causal_frame_tokens
+        self.debug = debug
         self.n, self.dim, self.heads = n, dim, heads
         self.head_dim = dim // heads
         self.device = torch.device(device)
@@ -131,6 +134,10 @@ class PrunedAttentionLayer:
 
     def forward_active(self, x_cur, n_active: int, *, fused=True, stream=None) -> None:
         """QKV of the selected tokens, cache sync, attention, scatter (after select)."""
+        if self.debug:
+            got = self._read_n_active(stream)
+            if got != n_active:
+                raise ValueError(f"forward_active: {n_active} active tokens given, the selection has {got}")
         if n_active == 0:
             return
         idx = self.idx
