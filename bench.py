@@ -203,40 +203,60 @@ def roofline_entry(kind, work, st, unit):
             "peak": PEAK_BF16_TFLOPS, "unit": unit, "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "ms": st}
 
 
-def hbm_kernels(tsa, torch, cfg, layer, xc, xp, reps=20):
+def hbm_kernels(tsa, torch, cfg, layer, xc, xp, sets=12, launches=20, reps=5):
     """The HBM-bound steps timed standalone: a1 score (all N rows of X_cur and X_ref read),
     a4 gather, a6 cache sync and a8 scatter of the N_a active rows (fused into the QKV and
-    attention kernels on the layer path).  The 256 MB MALL is flushed before every
-    repetition by reading a 512 MB buffer (reading, not writing: dirty flush lines
-    would be written back to HBM during the timed kernel)."""
-    stream = torch.cuda.current_stream()
+    attention kernels on the layer path).  Protocol: `launches` back-to-back launches per
+    event pair, cycling over `sets` copies of the inputs at distinct addresses (together more
+    than twice the 256 MB MALL, so each launch reads HBM), the median over `reps` pairs; per
+    launch = pair time / launches.  Beside each, a plain device copy of the same byte count
+    (half read, half written) timed the same way: the read+write rate the chip reaches on a
+    copy, for scale."""
     n, d, k = cfg.n, cfg.dim, cfg.n_active
-    flush = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device=xc.device)
-    scores = torch.empty(n, dtype=torch.float32, device=xc.device)
-    ka = torch.empty(k, d, dtype=torch.bfloat16, device=xc.device)
-    va = torch.empty_like(ka)
-    kc = layer.k_cache.clone()
-    vc = layer.v_cache.clone()
-    out = layer.out.clone()
+    dev = xc.device
+    stream = torch.cuda.current_stream()
     esz = xc.element_size()
+    g = torch.Generator(device="cpu").manual_seed(1)
+    xs = [(xc.clone(), xp.clone()) for _ in range(sets)]
+    idxs = [torch.randperm(n, generator=g)[:k].sort().values.to(torch.int32).to(dev) for _ in range(sets)]
+    kvs = [(layer.k_cache[:k].clone(), layer.v_cache[:k].clone()) for _ in range(sets)]
+    caches = [(layer.k_cache.clone(), layer.v_cache.clone()) for _ in range(sets)]
+    scores = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(sets)]
+    dsts = [torch.empty(k, d, dtype=xc.dtype, device=dev) for _ in range(sets)]
     ops = {
-        "a1_score": (lambda: tsa.token_scores(xc, xp, scores), 2 * n * d * esz + 4 * n),
-        "a4_gather": (lambda: tsa.gather_rows(xc, layer.idx, k, ka), k * d * (esz + 2)),
-        "a6_cache_sync": (lambda: tsa.kv_cache_sync(ka, va, layer.idx, k, kc, vc), 4 * k * d * 2),
-        "a8_scatter": (lambda: tsa.scatter_out(ka, layer.idx, k, out), 2 * k * d * 2),
+        "a1_score": (lambda i: tsa.token_scores(xs[i][0], xs[i][1], scores[i]), 2 * n * d * esz + 4 * n),
+        "a4_gather": (lambda i: tsa.gather_rows(xs[i][0], idxs[i], k, dsts[i]), k * d * (esz + 2)),
+        "a6_cache_sync": (lambda i: tsa.kv_cache_sync(kvs[i][0], kvs[i][1], idxs[i], k, caches[i][0], caches[i][1]),
+                          4 * k * d * 2),
+        "a8_scatter": (lambda i: tsa.scatter_out(kvs[i][0], idxs[i], k, caches[i][0]), 2 * k * d * 2),
     }
-    res = {}
-    for name, (fn, nbytes) in ops.items():
-        fn()
+
+    def per_launch_ms(fn):
+        for i in range(sets):
+            fn(i)
+        torch.cuda.synchronize()
         tm = EventTimer(torch, stream)
         for _ in range(reps):
-            flush.max()
             tm.start()
-            fn()
+            for j in range(launches):
+                fn(j % sets)
             tm.stop()
         torch.cuda.synchronize()
-        res[name] = roofline_entry("hbm", nbytes, stats(tm.times()), "GB/s")
-    del flush
+        return stats([t / launches for t in tm.times()])
+
+    res = {}
+    for name, (fn, nbytes) in ops.items():
+        st = per_launch_ms(fn)
+        half = nbytes // 2 // 2 * 2
+        src = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(sets)]
+        dst = [torch.empty_like(t) for t in src]
+        cst = per_launch_ms(lambda i: dst[i].copy_(src[i]))
+        del src, dst
+        e = roofline_entry("hbm", nbytes, st, "GB/s")
+        e["protocol"] = f"{launches} back-to-back launches per event pair over {sets} rotated input sets"
+        e["plain_copy_same_bytes"] = roofline_entry("hbm", 2 * half, cst, "GB/s")
+        res[name] = e
+    del xs, kvs, caches
     return res
 
 
@@ -299,15 +319,17 @@ def bench_step(args, torch, tsa, cfg):
         flops = int(4 * visible.sum() * cfg.head_dim * cfg.heads)
     dense = None
     if not args.no_dense:
-        # dense layer: the same QKV and attention kernels over every token, no selection
+        # dense layer: the same QKV and attention kernels over every token, no selection;
+        # each repetition synchronised on its own so that host-side gaps between
+        # repetitions are not timed
         layer.dense_forward(xc)
         torch.cuda.synchronize()
         td = EventTimer(torch, stream)
-        for _ in range(max(5, args.steps // 4)):
+        for _ in range(max(20, args.steps)):
             td.start()
             layer.dense_forward(xc)
             td.stop()
-        torch.cuda.synchronize()
+            torch.cuda.synchronize()
         dense = stats(td.times())
         layer.init_cache(xp)
 

@@ -7,10 +7,13 @@
 //
 // One wave moves R rows in 16-byte lanes (a 256-thread block: 4R rows).  All
 // loads of a pass (up to J slices per lane of each of the R rows, J sized to the
-// row) are issued before its stores.  Single-buffer copies of rows that fit one
-// pass of 4 slices per lane go two to a wave, so twice the bytes are in flight
-// (gather and scatter of 9828 rows of 1536 bf16 with a flushed MALL: 14 against
-// 17 us).  Copied sources are read with nontemporal loads: they are not read again.
+// row) are issued before its stores.  Copies of rows that fit one pass of 4
+// slices per lane go two to a wave, so twice the bytes are in flight (gather and
+// scatter of 9828 rows of 1536 bf16 with a flushed MALL: 14 against 17 us; the
+// two-buffer cache sync 21.6 against 22.4 us over back-to-back launches on
+// rotated inputs).  Copied sources are read with nontemporal loads (they are not
+// read again); the plain gather also stores nontemporally (11.8 against 12.5 us;
+// neutral for the scatter, slower for the two-buffer copy).
 #include "common.h"
 #include "kernels.h"
 
@@ -70,7 +73,7 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __rest
           if (RECOVER)
             out[q][c] = recover8(bc[q][j], be[q][RECOVER ? j : 0], one_m_s, sigma);
           else
-            out[q][c] = bc[q][j];
+            __builtin_nontemporal_store(bc[q][j], out[q] + c);
         }
       }
   }
@@ -164,10 +167,11 @@ hipError_t launch_gather_rows(const RowSource& src, long n, long dim, uint16_t* 
 template <int J, int R>
 static void copy_j(const uint16_t* a, const uint16_t* b, const int* rows, long n, uint16_t* da,
                    uint16_t* db, long dim, hipStream_t s) {
-  // two buffers (the cache sync) already put two rows' loads in flight per wave
+  // two buffers (the cache sync): R rows of each per wave as well
   if (b) {
-    const dim3 grid(static_cast<unsigned>((n + kWavesPerBlock - 1) / kWavesPerBlock));
-    hipLaunchKernelGGL((copy_rows_kernel<true, J, 1>), grid, dim3(256), 0, s, a, b, rows, n, da, db, dim);
+    constexpr long rows_per_block = kWavesPerBlock * R;
+    const dim3 grid(static_cast<unsigned>((n + rows_per_block - 1) / rows_per_block));
+    hipLaunchKernelGGL((copy_rows_kernel<true, J, R>), grid, dim3(256), 0, s, a, b, rows, n, da, db, dim);
   } else {
     constexpr long rows_per_block = kWavesPerBlock * R;
     const dim3 grid(static_cast<unsigned>((n + rows_per_block - 1) / rows_per_block));
