@@ -385,7 +385,8 @@ def bench_step(args, torch, tsa, cfg):
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": attention_traffic(),
+            # the counter summary covers the wan13b attention kernel only
+            "traffic": attention_traffic() if cfg.name == "wan13b" else None,
             "algorithmic_flop_per_launch": flops,
             # the shader clock the profiled attention kernel ran at (power-limited under full
             # MFMA load) and the fraction of the peak at that clock, next to the spec-clock frac
