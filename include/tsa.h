@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define TSA_ABI_VERSION 6
+#define TSA_ABI_VERSION 7
 
 typedef uint16_t tsa_bf16;
 
