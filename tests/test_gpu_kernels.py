@@ -485,6 +485,36 @@ def test_qkv_large_and_small_tiles_agree_bit_for_bit(kv_only, rope):
         assert torch.equal(a[pk], b)
 
 
+@pytest.mark.parametrize("n_x,m,dim,rope", [(3000, 2049, 1536, None), (12000, 11001, 3072, None),
+                                            (1500, 901, 768, (5, 12, 4))])
+def test_qkv_register_staged_and_lds_direct_agree_bit_for_bit(n_x, m, dim, rope):
+    """bf16 token rows go HBM -> LDS directly (qkv_gemm_lds_kernel); fp32 rows go through
+    registers and are converted on the way (qkv_gemm_kernel).  Fed the same values (fp32
+    rows that are exactly bf16), both kernels accumulate every output in the same order, so
+    Q, K and V (here written into cache rows, with rotary positions in one case) agree bit
+    for bit -- on the small-tile grid and, for 12000 x 3072, the large-tile grid."""
+    t = tsa()
+    g = torch.Generator().manual_seed(n_x)
+    xb = _randn_bf16(g, n_x, dim)
+    w = G.dev((torch.randn(3 * dim, dim, generator=g) / math.sqrt(dim)).to(torch.bfloat16))
+    rows = G.dev(torch.from_numpy(np.sort(np.random.default_rng(m).choice(n_x, m, replace=False)).astype(np.int32)))
+    heads = dim // 128 if dim % 128 == 0 else dim // 64
+    outs = []
+    for x in (G.dev(xb), G.dev(xb.float())):
+        q = torch.empty(m, dim, dtype=torch.bfloat16, device="cuda")
+        kc = torch.zeros(n_x, dim, dtype=torch.bfloat16, device="cuda")
+        vc = torch.zeros_like(kc)
+        if rope is None:
+            t.qkv_active(x, rows, m, w, q_out=q, k_out=kc, v_out=vc, out_is_cache=True, n_cache=n_x)
+        else:
+            t.qkv_active_rope(x, rows, m, w, heads, rope[0], rope[1], q_out=q, k_out=kc, v_out=vc,
+                              out_is_cache=True, n_cache=n_x)
+        torch.cuda.synchronize()
+        outs.append((q, kc, vc))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
 @pytest.mark.parametrize("n_x,m,dim,rope", [(2000, 777, 1536, None), (9000, 7461, 3072, None),
                                             (1200, 500, 512, (6, 10, 4))])
 def test_rows_to_cache_equals_fused_recovery(n_x, m, dim, rope):

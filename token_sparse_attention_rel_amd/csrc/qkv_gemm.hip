@@ -50,9 +50,10 @@ struct GemmTile {
   static constexpr int kLoadA = kBN / kLoadRows;      // 16-byte A chunks per thread and K step
   static constexpr int kMinBlocks = MIN_BLOCKS;       // resident workgroups per CU
 };
-// 256 x 256 on 8 waves of 64 x 128 (144 KB of LDS, one workgroup per CU) for grids that
-// fill the chip several times; 128 x 128 on 4 waves of 64 x 64 (72 KB, two per CU) for
-// smaller ones, where the large tile's last wave of workgroups would leave CUs idle.
+// 256 x 256 on 8 waves of 64 x 128 (one workgroup per CU; LDS: 144 KB register-staged with
+// padded rows, 128 KB LDS-direct with unpadded swizzled rows) for grids that fill the chip
+// several times; 128 x 128 on 4 waves of 64 x 64 (72 / 64 KB, two per CU) for smaller ones,
+// where the large tile's last wave of workgroups would leave CUs idle.
 using TileLarge = GemmTile<4, 2, 2, 4, 1>;
 using TileSmall = GemmTile<2, 2, 2, 2, 2>;
 // The large tile is used from this many workgroups on (four per CU of a 256-CU chip).
