@@ -1,5 +1,8 @@
 """Driver of one pruned attention layer on one GPU: owns the persistent buffers
-and sequences the C-ABI calls.  No arithmetic happens here.
+and sequences the C-ABI calls.  Token data is never touched on the host; the
+only arithmetic here is scalar bookkeeping: the HSA schedule's active count per
+step (the sum of the group sizes whose period divides the step, which sizes the
+calls) and the Euler step sigma_{i+1} - sigma_i handed to the update kernel.
 
 A step (HSA page §2.2) is: score + select + compact (select_active), QKV of
 the active tokens with their K/V written straight into the cache rows
