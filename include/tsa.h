@@ -176,8 +176,9 @@ tsa_status tsa_assign_groups(const float* scores, int64_t n, int n_groups,
  *                to row rows[r] (rows required, each < n_cache) -- this fuses
  *                the cache sync (a6) into the projection.
  *   eps          device bf16 [n_x_rows, dim] or NULL (no recovery).
- * dim must be a multiple of 64; n_x_rows*dim*2 and 3*dim*dim*2 must each be below
- * 2^31 bytes (32-bit buffer ranges).
+ * dim must be a multiple of 64; 3*dim*dim*2 must be below 2^31 bytes (the weight
+ * is one 32-bit buffer range).  x of any size (token rows of 2^31 bytes or more
+ * are read through 64-bit addresses).
  * Errors: INVALID_ARG, SHAPE, DTYPE, ALIGNMENT, HIP.
  */
 tsa_status tsa_qkv_active(const void* x, int x_dtype, int64_t n_x_rows, const int32_t* rows,
@@ -220,7 +221,7 @@ tsa_status tsa_qkv_active_rope(const void* x, int x_dtype, int64_t n_x_rows, con
  *   w_qkv      as in tsa_qkv_active.
  *   k_cache, v_cache  device bf16 [n_cache, dim].
  *   heads, height, width, rope_base  rotary positions (heads = 0: none).
- * dim a multiple of 64; n*dim*2 and 3*dim*dim*2 below 2^31 bytes.
+ * dim a multiple of 64; 3*dim*dim*2 below 2^31 bytes; a of any size.
  * Errors: INVALID_ARG, SHAPE, ALIGNMENT, HIP.
  */
 tsa_status tsa_qkv_rows_to_cache(const tsa_bf16* a, int64_t n, int64_t dim, const int32_t* rows,
@@ -266,7 +267,8 @@ tsa_status tsa_kv_cache_sync(const tsa_bf16* k_a, const tsa_bf16* v_a, const int
  *            the same stream combines them.  NULL: no split.  Results agree to
  *            rounding; the workspace keeps nothing between calls, and calls that
  *            run concurrently need separate workspaces.
- * n_kv*heads*head_dim*2 must be below 2^31 bytes (32-bit buffer range of the cache).
+ * Any cache size up to n_kv < 2^31 rows: caches of 2^31 bytes or more run kernels
+ * that rebase their 32-bit buffer ranges at every key tile.
  * Errors: INVALID_ARG, SHAPE, ALIGNMENT, WORKSPACE (workspace non-NULL and
  * workspace_bytes below the required size), HIP.
  */

@@ -103,9 +103,10 @@ def test_qkv_validation():
     assert qkv(w=U) == B.ERR_ALIGNMENT
     assert qkv(eps=A, sigma=float("nan")) == B.ERR_INVALID_ARG
     assert qkv(rows=A + 2) == B.ERR_ALIGNMENT
-    # 32-bit buffer ranges: 2^20 rows of 1024 bf16 = 2 GiB is one byte too many
-    assert qkv(nx=1 << 20, dim=1024) == B.ERR_SHAPE
-    assert qkv(dim=19008) == B.ERR_SHAPE  # 3*D*D*2 >= 2^31
+    # token rows of 2 GiB and more are accepted (64-bit row addresses); n = 0 launches nothing
+    assert qkv(nx=1 << 20, dim=1024, n=0) == B.OK
+    assert qkv(nx=(1 << 31) - 1, dim=4096, n=0) == B.OK
+    assert qkv(dim=19008) == B.ERR_SHAPE  # the weight is one 32-bit buffer range: 3*D*D*2 >= 2^31
 
 
 def attn(**kw):
@@ -128,7 +129,10 @@ def test_attention_validation():
     assert attn(scale=float("inf")) == B.ERR_INVALID_ARG
     assert attn(k=U) == B.ERR_ALIGNMENT
     assert attn(lse=A + 2) == B.ERR_ALIGNMENT
-    assert attn(nkv=1 << 20, heads=8, hd=128) == B.ERR_SHAPE  # cache of 2 GiB
+    # caches of 2 GiB and more are accepted (buffer ranges rebased per key tile); n_q = 0 launches nothing
+    assert attn(nkv=1 << 20, heads=8, hd=128, nq=0) == B.OK
+    assert attn(nkv=(1 << 31) - 1, heads=64, hd=128, nq=0) == B.OK
+    assert attn(nkv=1 << 31, heads=8, hd=128, nq=0) == B.ERR_SHAPE  # rows past 2^31 - 1
     assert attn(ws=U, ws_bytes=1 << 20) == B.ERR_ALIGNMENT
     assert attn(nq=0, ws=A, ws_bytes=0) == B.OK
     f = lib()
@@ -270,3 +274,4 @@ def test_qkv_rows_to_cache_validation():
     assert rc(heads=2, h=4, w_=4, base=0.0) == B.ERR_INVALID_ARG
     assert rc(a=U) == B.ERR_ALIGNMENT
     assert rc(rows=A + 2) == B.ERR_ALIGNMENT
+    assert rc(dim=19008) == B.ERR_SHAPE  # 3*D*D*2 >= 2^31

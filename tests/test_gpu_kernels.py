@@ -340,22 +340,22 @@ def test_qkv_matches_oracle(n_x, m, dim, src):
     assert torch.equal(kch[rows], k.cpu()) and torch.equal(vch[rows], v.cpu())
 
 
-@pytest.mark.slow
-@pytest.mark.parametrize("src", ["bf16", "recover"])
-def test_qkv_at_the_buffer_range_limit(src):
-    """Token rows at the end of the largest input the ABI accepts (n_x * dim * 2 bytes just
-    under 2**31, 699050 rows of 1536): the 32-bit offsets of the row loads (and of the noise
-    rows) run at their limit; K/V written into caches of the same size."""
+def _qkv_rows_up_to(n_x, src, seed):
+    """Token rows at the end of an input of n_x rows of 1536 (bf16 or fp32 rows, or LIPAR's
+    recovery rows from clean and noise rows of the same size): sampled rows against the oracle,
+    K/V written into caches of n_x rows, untouched cache rows left zero."""
     t = tsa()
     dim = 1536
-    n_x = (2 ** 31 - 1) // (dim * 2)
-    gen = torch.Generator(device="cuda").manual_seed(7)
-    x = torch.randn(n_x, dim, device="cuda", generator=gen).to(torch.bfloat16)
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    x = torch.randn(n_x, dim, device="cuda", generator=gen)
+    if src != "f32":
+        x = x.to(torch.bfloat16)
     w = (torch.randn(3 * dim, dim, device="cuda", generator=gen) / math.sqrt(dim)).to(torch.bfloat16)
-    rng = np.random.default_rng(7)
+    rng = np.random.default_rng(seed)
     rows = np.unique(np.concatenate([np.arange(16), np.arange(n_x - 300, n_x),
                                      rng.choice(n_x, 700, replace=False)])).astype(np.int32)
     m = rows.size
+    print(f"  n_x={n_x} ({n_x * dim * x.element_size()} bytes of {src} rows), {m} rows", flush=True)
     rd = G.dev(torch.from_numpy(rows))
     q = torch.empty(m, dim, dtype=torch.bfloat16, device="cuda")
     k = torch.empty_like(q)
@@ -383,16 +383,68 @@ def test_qkv_at_the_buffer_range_limit(src):
     for name, got in (("q", q), ("k", k), ("v", v)):
         gh = G.host64(got)
         if src == "recover":
-            G.assert_close(gh, want[name], f"range limit {src} {name}")
+            G.assert_close(gh, want[name], f"{n_x} rows {src} {name}")
         else:
             part = "qkv".index(name)
             wp = np.abs(G.host64(w)[part * dim:(part + 1) * dim])
             G.assert_projection_close(gh, want[name], np.abs(ref.round_bf16(a_rows)) @ wp.T, dim,
-                                      f"range limit {src} {name}")
+                                      f"{n_x} rows {src} {name}")
     rl = torch.from_numpy(rows).long().cuda()
     assert torch.equal(kc[rl], k) and torch.equal(vc[rl], v)
     others = torch.from_numpy(np.setdiff1d(rng.choice(n_x, 2000, replace=False), rows)).long().cuda()
     assert not kc[others].any() and not vc[others].any()
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("src", ["bf16", "recover"])
+def test_qkv_at_the_buffer_range_limit(src):
+    """The largest bf16 input one 32-bit buffer range holds (n_x * dim * 2 bytes just under
+    2**31, 699050 rows of 1536): the 32-bit offsets of the row loads (and of the noise rows)
+    run at their limit."""
+    _qkv_rows_up_to((2 ** 31 - 1) // (1536 * 2), src, 7)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("src", ["bf16", "recover", "f32"])
+def test_qkv_past_the_buffer_range_limit(src):
+    """800000 token rows of 1536 (2.46 GB of bf16 rows, 4.9 GB of fp32 ones): bf16 rows take
+    the kernels that address every row with a 64-bit pointer (LDS-direct copies from global
+    addresses; plain loads of the clean and noise rows for the recovery), with sampled rows
+    past the 2 GiB mark."""
+    _qkv_rows_up_to(800_000, src, 8)
+
+
+@pytest.mark.slow
+def test_rows_to_cache_past_the_buffer_range_limit():
+    """tsa_qkv_rows_to_cache with 800000 compact rows of 1536 (2.46 GB) into caches of 1000000
+    rows: the compact rows past the 2 GiB mark are read through 64-bit addresses; sampled rows
+    against the oracle, their cache rows bit-identical to the compact projection's."""
+    t = tsa()
+    dim, n, n_cache = 1536, 800_000, 1_000_000
+    gen = torch.Generator(device="cuda").manual_seed(9)
+    a = torch.randn(n, dim, device="cuda", generator=gen).to(torch.bfloat16)
+    w = (torch.randn(3 * dim, dim, device="cuda", generator=gen) / math.sqrt(dim)).to(torch.bfloat16)
+    rng = np.random.default_rng(9)
+    rows = np.sort(rng.choice(n_cache, n, replace=False)).astype(np.int32)
+    kc = torch.zeros(n_cache, dim, dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    t.qkv_rows_to_cache(a, G.dev(torch.from_numpy(rows)), n, w, kc, vc)
+    torch.cuda.synchronize()
+    sample = np.unique(np.concatenate([np.arange(8), np.arange(n - 200, n), rng.choice(n, 500, replace=False)]))
+    a_rows = G.host64(a[torch.from_numpy(sample).long().cuda()])
+    want = ref.project(a_rows, G.host64(w), parts="kv")
+    cr = torch.from_numpy(rows[sample]).long().cuda()
+    for name, cache in (("k", kc), ("v", vc)):
+        part = "qkv".index(name)
+        wp = np.abs(G.host64(w)[part * dim:(part + 1) * dim])
+        G.assert_projection_close(G.host64(cache[cr]), want[name], np.abs(a_rows) @ wp.T, dim,
+                                  f"rows_to_cache past 2 GiB {name}")
+    # the same rows through the compact projection: bit-identical
+    sub = torch.from_numpy(sample.astype(np.int32))
+    ks = torch.empty(sample.size, dim, dtype=torch.bfloat16, device="cuda")
+    vs = torch.empty_like(ks)
+    t.qkv_active(a, G.dev(sub), sample.size, w, k_out=ks, v_out=vs)
+    assert torch.equal(kc[cr], ks) and torch.equal(vc[cr], vs)
 
 
 @pytest.mark.parametrize("src", ["bf16", "recover", "f32"])
@@ -623,6 +675,54 @@ def test_attention_at_the_buffer_range_limit():
         t.sparse_query_attention(q, k, v, n_q, heads, hd, out, workspace=w)
         torch.cuda.synchronize()
         G.assert_close(G.host64(out)[rows], want, f"attention at the range limit, {name}")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("heads,hd", [(1, 128), (2, 64)])
+def test_attention_past_the_buffer_range_limit(heads, hd):
+    """K/V caches of 12000000 keys of 128 bf16 (3.07 GB each): the kernels for caches past one
+    32-bit buffer range, which place the range at every key tile's first row.  The keys past the
+    2 GiB mark (30 % of them) carry +3 on channel 0 of each head and their values +2, and the
+    queries +-2 on that channel, so every output depends on reading those rows right.  Whole
+    tiles, the split schedule, and the frame-causal variant with frames of 4000000 keys (queries
+    of frames 0 and 1 see no key past the mark, those of frame 2 all of them); sampled query rows
+    against the oracle."""
+    t = tsa()
+    dim = heads * hd
+    n_kv, n_q, frame = 12_000_000, 300, 4_000_000
+    mark = 2 ** 31 // (dim * 2)  # first key row at or past 2 GiB
+    gen = torch.Generator(device="cuda").manual_seed(41 + hd)
+    ch0 = torch.arange(heads, device="cuda") * hd
+    q = torch.randn(n_q, dim, device="cuda", generator=gen)
+    q[:, ch0] = torch.where(torch.arange(n_q, device="cuda") % 2 == 0, 2.0, -2.0)[:, None]
+    q = q.to(torch.bfloat16)
+    k = torch.randn(n_kv, dim, device="cuda", generator=gen)
+    k[mark:, ch0] += 3.0
+    k = k.to(torch.bfloat16)
+    v = torch.randn(n_kv, dim, device="cuda", generator=gen)
+    v[mark:] += 2.0
+    v = v.to(torch.bfloat16)
+    rows = np.array([0, 1, 2, 150, 255, 256, 298, 299])
+    q_tokens = (np.arange(n_q) % 3) * frame + np.arange(n_q)  # frames 0, 1, 2 in turn
+    print(f"  heads={heads} hd={hd} n_kv={n_kv} ({n_kv * dim * 2} bytes per cache, mark at key {mark}); "
+          f"oracle on rows {rows.tolist()}", flush=True)
+    k64, v64 = G.host64(k), G.host64(v)
+    q64 = G.host64(q)[rows]
+    want = ref.attention(q64, k64, v64, heads)
+    want_c = ref.attention_frame_causal(q64, k64, v64, heads, q_tokens[rows], frame)
+    del k64, v64
+    ws_bytes = t.attention_workspace_bytes(n_q, n_kv, heads, hd)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    for name, w in (("whole tiles", None), ("split", ws if ws_bytes > 0 else None)):
+        out = torch.empty(n_q, dim, dtype=torch.bfloat16, device="cuda")
+        t.sparse_query_attention(q, k, v, n_q, heads, hd, out, workspace=w)
+        torch.cuda.synchronize()
+        G.assert_close(G.host64(out)[rows], want, f"attention past 2 GiB, {name}")
+    out = torch.empty(n_q, dim, dtype=torch.bfloat16, device="cuda")
+    t.frame_causal_attention(q, k, v, n_q, heads, hd, G.dev(torch.from_numpy(q_tokens.astype(np.int32))),
+                             frame, out)
+    torch.cuda.synchronize()
+    G.assert_close(G.host64(out)[rows], want_c, "frame-causal attention past 2 GiB")
 
 
 # Split schedule: shapes whose last round of query tiles (256 queries for head_dim 128, 128

@@ -10,7 +10,9 @@
 // head.
 // Key/value tiles of 32 rows are staged row-major through rings of four LDS
 // slots, two tiles per barrier; the next pair's global loads are in flight
-// while the current pair is computed.
+// while the current pair is computed.  They arrive through range-checked buffer
+// loads with 32-bit offsets: a K or V cache of 2 GiB or more takes kernels
+// that place the buffer range at each tile's first row.
 //
 // Layout trick: the score tile is computed transposed, S^T = K Q^T, with
 // v_mfma_f32_32x32x16_bf16.  In that instruction's accumulator layout a lane
@@ -97,6 +99,8 @@ constexpr float kLazyMax = 8.0f;
 // Word 3 of a raw buffer resource on gfx9-class GPUs (32-bit elements, no swizzle);
 // out-of-range offsets then read as zero.
 constexpr int kBufferRsrcFlags = 0x00020000;
+// Largest byte range one buffer resource describes here (its offsets are 32-bit).
+constexpr long kMaxRangeBytes = 0x7FFFFFFF;
 
 template <bool B>
 using Flag = std::integral_constant<bool, B>;
@@ -111,7 +115,7 @@ constexpr long attn_piece_floats() { return attn_blocks<HD>() * 64L * (HD / 32 *
 // normalise and write the bf16 output rows (+ LSE); otherwise write the partial
 // (unnormalised O, shift, sum) to `part` for a later merge.  ks / vs are the
 // four-slot LDS rings of K and V tiles (tile t in slot (t - t0) mod 4).
-template <int HD, bool CAUSAL = false>
+template <int HD, bool CAUSAL = false, bool BIG = false>
 __device__ __forceinline__ void attend_segment(const AttnArgs& a, uint16_t* ks_base, uint16_t* vs_base,
                                                long tile, long t0, long t1, float* part) {
   constexpr int BN = kAttnBN;
@@ -201,11 +205,20 @@ __device__ __forceinline__ void attend_segment(const AttnArgs& a, uint16_t* ks_b
 
   // K/V tiles are fetched with range-checked buffer loads: rows past the end
   // of the cache read as zeros, so prefetches beyond the last tile need no branch.
-  const int kv_bytes = static_cast<int>(((n_kv - 1) * D + HD) * 2);
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(a.k + head * HD), 0, kv_bytes, kBufferRsrcFlags);
-  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(a.v + head * HD), 0, kv_bytes, kBufferRsrcFlags);
+  // A head's K/V below 2 GiB is one buffer range, the tile's first row its offset;
+  // a larger cache (BIG) gets a range based at each tile's first row instead.
+  struct KvSrc {
+    __amdgpu_buffer_rsrc_t rs;
+    const uint16_t* base;  // the head's first element
+  };
+  const long kv_elems = (n_kv - 1) * D + HD;  // from the head's first element to its last
+  const int kv_bytes = static_cast<int>(BIG ? kMaxRangeBytes : kv_elems * 2);
+  const KvSrc krs{__builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.k + head * HD), 0, kv_bytes,
+                                                    kBufferRsrcFlags),
+                  a.k + head * HD};
+  const KvSrc vrs{__builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.v + head * HD), 0, kv_bytes,
+                                                    kBufferRsrcFlags),
+                  a.v + head * HD};
   // Loader: chunk id = tid + NT*j covers row id / CPR, 16-byte column id % CPR.
   int g_off[NCH];
   uint32_t k_lds[NCH], v_lds[NCH];
@@ -216,12 +229,24 @@ __device__ __forceinline__ void attend_segment(const AttnArgs& a, uint16_t* ks_b
     k_lds[j] = (id / CPR) * LDK + (id % CPR) * 8;
     v_lds[j] = (id / CPR) * LDV + (id % CPR) * 8;
   }
-  auto gload = [&](u32x4* r, __amdgpu_buffer_rsrc_t rs, long kv0) {
-    const long boff = kv0 * D * 2;
-    const int so = boff < kv_bytes ? static_cast<int>(boff) : kv_bytes;
+  auto gload = [&](u32x4* r, const KvSrc& src, long kv0) {
+    if constexpr (BIG) {
+      // bytes from row kv0 to the end of the head's last row; none left: every load reads zero
+      const long e0 = kv0 * D;
+      const long rem = (kv_elems - e0) * 2;
+      const int nrec = rem <= 0 ? 0 : rem > kMaxRangeBytes ? static_cast<int>(kMaxRangeBytes) : static_cast<int>(rem);
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(src.base + (rem > 0 ? e0 : 0)), 0, nrec, kBufferRsrcFlags);
 #pragma unroll
-    for (int j = 0; j < NCH; ++j)
-      r[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, g_off[j], so, 0));
+      for (int j = 0; j < NCH; ++j)
+        r[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, g_off[j], 0, 0));
+    } else {
+      const long boff = kv0 * D * 2;
+      const int so = boff < kv_bytes ? static_cast<int>(boff) : kv_bytes;
+#pragma unroll
+      for (int j = 0; j < NCH; ++j)
+        r[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(src.rs, g_off[j], so, 0));
+    }
   };
   auto sstore = [&](uint16_t* buf, const uint32_t* off, const u32x4* r) {
 #pragma unroll
@@ -492,13 +517,13 @@ __device__ __forceinline__ void attend_segment(const AttnArgs& a, uint16_t* ks_b
   }
 }
 
-template <int HD>
+template <int HD, bool BIG>
 __global__ __launch_bounds__(64 * attn_waves<HD>(), attn_min_blocks<HD>()) void attention_kernel(AttnArgs a) {
   __shared__ __align__(16) uint16_t ks[4 * kAttnBN * (HD + 8)];
   __shared__ __align__(16) uint16_t vs[4 * kAttnBN * (HD + 32)];
   const long n_qt = (a.n_q + attn_rows<HD>() - 1) / attn_rows<HD>();
   const long tile = xcd_remap(blockIdx.x, n_qt * a.heads);
-  attend_segment<HD>(a, ks, vs, tile, 0, (a.n_kv + kAttnBN - 1) / kAttnBN, nullptr);
+  attend_segment<HD, false, BIG>(a, ks, vs, tile, 0, (a.n_kv + kAttnBN - 1) / kAttnBN, nullptr);
 }
 
 // Frame-causal variant: one workgroup per query tile, over the key tiles its
@@ -507,14 +532,14 @@ __global__ __launch_bounds__(64 * attn_waves<HD>(), attn_min_blocks<HD>()) void 
 // tile before the next: the long tiles start first on every XCD and the short
 // ones fill in behind them (a longest-first schedule; with the XCD-contiguous
 // order of the bidirectional kernel one XCD got far more work than another).
-template <int HD>
+template <int HD, bool BIG>
 __global__ __launch_bounds__(64 * attn_waves<HD>(), attn_min_blocks<HD>()) void attention_causal_kernel(AttnArgs a) {
   __shared__ __align__(16) uint16_t ks[4 * kAttnBN * (HD + 8)];
   __shared__ __align__(16) uint16_t vs[4 * kAttnBN * (HD + 32)];
   const long n_qt = (a.n_q + attn_rows<HD>() - 1) / attn_rows<HD>();
   const long b = blockIdx.x;
   const long tile = (b % a.heads) * n_qt + (n_qt - 1 - b / a.heads);
-  attend_segment<HD, true>(a, ks, vs, tile, 0, (a.n_kv + kAttnBN - 1) / kAttnBN, nullptr);
+  attend_segment<HD, true, BIG>(a, ks, vs, tile, 0, (a.n_kv + kAttnBN - 1) / kAttnBN, nullptr);
 }
 
 // Split schedule for the last, partly filled round of query tiles.  With C
@@ -525,7 +550,7 @@ __global__ __launch_bounds__(64 * attn_waves<HD>(), attn_min_blocks<HD>()) void 
 // attention_merge_kernel combines them.  Pieces are numbered key-range-major
 // and dealt to XCDs in contiguous runs, so the workgroups resident on one XCD
 // at a time read the same key range of the same head and share its L2.
-template <int HD>
+template <int HD, bool BIG>
 __global__ __launch_bounds__(64 * attn_waves<HD>(), attn_min_blocks<HD>()) void attention_split_kernel(AttnArgs a, float* ws,
                                                                                    long full, long tail,
                                                                                    int kp) {
@@ -534,13 +559,13 @@ __global__ __launch_bounds__(64 * attn_waves<HD>(), attn_min_blocks<HD>()) void 
   const long n_t = (a.n_kv + kAttnBN - 1) / kAttnBN;
   const long b = blockIdx.x;
   if (b < full) {
-    attend_segment<HD>(a, ks, vs, xcd_remap(b, full), 0, n_t, nullptr);
+    attend_segment<HD, false, BIG>(a, ks, vs, xcd_remap(b, full), 0, n_t, nullptr);
     return;
   }
   const long p = xcd_remap(b - full, tail * kp);
   const long j = p / tail, i = p - j * tail;
-  attend_segment<HD>(a, ks, vs, full + i, j * n_t / kp, (j + 1) * n_t / kp,
-                     ws + (i * kp + j) * attn_piece_floats<HD>());
+  attend_segment<HD, false, BIG>(a, ks, vs, full + i, j * n_t / kp, (j + 1) * n_t / kp,
+                                 ws + (i * kp + j) * attn_piece_floats<HD>());
 }
 
 // One workgroup per cut tile: O = sum_j w_j O_j / sum_j w_j l_j with
@@ -603,7 +628,7 @@ long resident_ctas() {
   }
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attention_split_kernel<HD>,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attention_split_kernel<HD, false>,
                                                    64 * attn_waves<HD>(), 0) != hipSuccess)
     return 0;
   const int c = cus * (per_cu > 0 ? per_cu : 1);
@@ -662,18 +687,23 @@ size_t split_bytes(const SplitPlan& sp) {
   return static_cast<size_t>(sp.tail) * sp.kp * attn_piece_floats<HD>() * sizeof(float);
 }
 
-template <int HD>
+// K/V of one head span more bytes than one buffer resource addresses.
+bool big_kv(const AttnArgs& a, int hd) {
+  return ((a.n_kv - 1) * a.heads * static_cast<long>(hd) + hd) * 2 > kMaxRangeBytes;
+}
+
+template <int HD, bool BIG>
 hipError_t launch_hd(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t s) {
   const SplitPlan sp = ws ? split_plan<HD>(a.n_q, a.n_kv, a.heads) : SplitPlan{};
   const dim3 block(64 * attn_waves<HD>());
   if (sp.kp == 1) {
-    hipLaunchKernelGGL(attention_kernel<HD>, dim3(static_cast<unsigned>(query_tiles<HD>(a.n_q, a.heads))),
+    hipLaunchKernelGGL((attention_kernel<HD, BIG>), dim3(static_cast<unsigned>(query_tiles<HD>(a.n_q, a.heads))),
                        block, 0, s, a);
     return hipGetLastError();
   }
   if (ws_bytes < split_bytes<HD>(sp)) return hipErrorInvalidValue;
   float* w = static_cast<float*>(ws);
-  hipLaunchKernelGGL(attention_split_kernel<HD>, dim3(static_cast<unsigned>(sp.full + sp.tail * sp.kp)),
+  hipLaunchKernelGGL((attention_split_kernel<HD, BIG>), dim3(static_cast<unsigned>(sp.full + sp.tail * sp.kp)),
                      block, 0, s, a, w, sp.full, sp.tail, sp.kp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -706,13 +736,17 @@ hipError_t launch_attention_causal(const uint16_t* q, const uint16_t* k, const u
   a.lse = lse;
   a.q_tokens = q_tokens;
   a.frame_tokens = frame_tokens;
-  if (head_dim == 128) {
-    hipLaunchKernelGGL(attention_causal_kernel<128>, dim3(static_cast<unsigned>(query_tiles<128>(n_q, heads))),
-                       dim3(64 * attn_waves<128>()), 0, s, a);
-  } else {
-    hipLaunchKernelGGL(attention_causal_kernel<64>, dim3(static_cast<unsigned>(query_tiles<64>(n_q, heads))),
-                       dim3(64 * attn_waves<64>()), 0, s, a);
-  }
+  const bool big = big_kv(a, head_dim);
+  const dim3 grid128(static_cast<unsigned>(query_tiles<128>(n_q, heads))), block128(64 * attn_waves<128>());
+  const dim3 grid64(static_cast<unsigned>(query_tiles<64>(n_q, heads))), block64(64 * attn_waves<64>());
+  if (head_dim == 128 && big)
+    hipLaunchKernelGGL((attention_causal_kernel<128, true>), grid128, block128, 0, s, a);
+  else if (head_dim == 128)
+    hipLaunchKernelGGL((attention_causal_kernel<128, false>), grid128, block128, 0, s, a);
+  else if (big)
+    hipLaunchKernelGGL((attention_causal_kernel<64, true>), grid64, block64, 0, s, a);
+  else
+    hipLaunchKernelGGL((attention_causal_kernel<64, false>), grid64, block64, 0, s, a);
   return hipGetLastError();
 }
 
@@ -731,7 +765,9 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t
   a.out = out;
   a.out_rows = out_rows;
   a.lse = lse;
-  return head_dim == 128 ? launch_hd<128>(a, ws, ws_bytes, s) : launch_hd<64>(a, ws, ws_bytes, s);
+  if (big_kv(a, head_dim))
+    return head_dim == 128 ? launch_hd<128, true>(a, ws, ws_bytes, s) : launch_hd<64, true>(a, ws, ws_bytes, s);
+  return head_dim == 128 ? launch_hd<128, false>(a, ws, ws_bytes, s) : launch_hd<64, false>(a, ws, ws_bytes, s);
 }
 
 }  // namespace tsa

@@ -27,7 +27,9 @@
 // while the current one is multiplied); rows that need arithmetic on the way (the
 // recovery blend, fp32 input) go through registers, loaded two K steps ahead
 // (qkv_gemm_kernel).  All rows arrive through
-// range-checked buffer loads (invalid rows read as zeros, no per-step selects).
+// range-checked buffer loads (invalid rows read as zeros, no per-step selects);
+// token rows of 2 GiB or more (whose byte offsets exceed the buffer loads' 32 bits)
+// take kernel variants (BIG) that address every row with a 64-bit pointer instead.
 #include "common.h"
 #include "kernels.h"
 
@@ -119,6 +121,8 @@ __device__ __forceinline__ void rope_pair(const GemmArgs& a, const float pos[3],
 constexpr int kBufferRsrcFlags = 0x00020000;
 // A per-lane offset that is always out of range: the load returns zeros.
 constexpr int kOutOfRange = 0x7FFFFFF0;
+// Largest byte range one buffer resource describes here (its offsets are 32-bit).
+constexpr long kMaxRangeBytes = 0x7FFFFFFF;
 
 // Token tiles handled together per XCD: the workgroups that run at the same
 // time on one XCD then share few W panels and few token tiles in its L2.
@@ -199,9 +203,10 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, const f32x16 (&acc
 // Rows that need arithmetic on the way (the recovery blend, fp32 input): staged
 // through registers, loaded two K steps ahead and converted when stored to padded
 // LDS rows one step ahead.
-template <int SRC, typename TL>
+template <int SRC, typename TL, bool BIG = false>
 __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void qkv_gemm_kernel(GemmArgs a) {
   static_assert(SRC == kSrcRecover || SRC == kSrcF32, "bf16 rows take qkv_gemm_lds_kernel");
+  static_assert(!BIG || SRC == kSrcRecover, "fp32 rows are always read through 64-bit pointers");
   constexpr int kGemmBM = TL::kBM, kGemmBN = TL::kBN, kGemmWavesT = TL::kWavesT;
   constexpr int kWaveBF = TL::kBF, kWaveBT = TL::kBT;
   constexpr int kLoadRows = TL::kLoadRows, kLoadW = TL::kLoadW, kLoadA = TL::kLoadA;
@@ -230,7 +235,11 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void qkv_gemm_kernel(
       kBufferRsrcFlags);
   int w_off[kLoadW], x_off[kLoadA], e_off[kLoadA];
   long ftok[kLoadA];
-  bool tvalid[kLoadA];
+  bool tvalid[kLoadA], tclean[kLoadA];
+  // BIG recovery rows: 64-bit pointers to the clean and noise chunks (row 0 when the
+  // row has none; the value read is then replaced by zeros)
+  const uint16_t* xp[BIG ? kLoadA : 1];
+  const uint16_t* ep[BIG ? kLoadA : 1];
 #pragma unroll
   for (int j = 0; j < kLoadW; ++j) {
     const long c = c_base + lrow + kLoadRows * j;
@@ -245,9 +254,17 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void qkv_gemm_kernel(
     if constexpr (SRC == kSrcRecover) {
       const long src = tok - a.src_off;
       const bool clean = tvalid[j] && src >= 0 && src < a.n_x_rows;
-      x_off[j] = clean ? static_cast<int>((src * dim + lcol) * 2) : kOutOfRange;
-      e_off[j] = tvalid[j] ? static_cast<int>((tok * dim + lcol) * 2) : kOutOfRange;
+      tclean[j] = clean;
+      if constexpr (BIG) {
+        xp[j] = static_cast<const uint16_t*>(a.x) + (clean ? src : 0) * dim + lcol;
+        ep[j] = a.eps + tok * dim + lcol;
+        x_off[j] = e_off[j] = 0;
+      } else {
+        x_off[j] = clean ? static_cast<int>((src * dim + lcol) * 2) : kOutOfRange;
+        e_off[j] = tvalid[j] ? static_cast<int>((tok * dim + lcol) * 2) : kOutOfRange;
+      }
     } else {
+      tclean[j] = false;
       x_off[j] = tvalid[j] ? static_cast<int>((tok * dim + lcol) * 2) : kOutOfRange;
       e_off[j] = kOutOfRange;
     }
@@ -265,6 +282,11 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void qkv_gemm_kernel(
         const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(a.x) + ftok[j] * dim + k0 + lcol);
         araw[j][0] = __builtin_bit_cast(u32x4, p[0]);
         araw[j][1] = __builtin_bit_cast(u32x4, p[1]);
+      } else if constexpr (BIG) {
+        const u32x4 c = *reinterpret_cast<const u32x4*>(xp[j] + k0);
+        const u32x4 e = *reinterpret_cast<const u32x4*>(ep[j] + k0);
+        araw[j][0] = tclean[j] ? c : u32x4{0u, 0u, 0u, 0u};
+        araw[j][1] = tvalid[j] ? e : u32x4{0u, 0u, 0u, 0u};
       } else {
         araw[j][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, x_off[j], so, 0));
         araw[j][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ers, e_off[j], so, 0));
@@ -339,6 +361,12 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void qkv_gemm_kernel(
 __device__ __forceinline__ void lds_copy16(__amdgpu_buffer_rsrc_t rs, uint16_t* lds, int voff, int soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
 }
+// The same copy from a 64-bit address per lane (rows past one buffer range).  (A
+// helper of its own: written straight into a kernel template's lambda, the builtin
+// keeps the host compiler from emitting that kernel's launch stub.)
+__device__ __forceinline__ void lds_copy16_global(const uint16_t* src, uint16_t* lds) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
 // Wait until every copy this wave issued has landed in LDS (vmcnt 0).
 __device__ __forceinline__ void lds_copy_wait() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
@@ -350,7 +378,7 @@ __device__ __forceinline__ void lds_copy_wait() { __builtin_amdgcn_s_waitcnt(0x0
 // is copied into the buffer not being multiplied while the other one is, and every
 // buffer is an LDS array of its own, so the only waits for the copies are at the
 // barrier that ends the step.
-template <typename TL>
+template <typename TL, bool BIG = false>
 __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void qkv_gemm_lds_kernel(GemmArgs a) {
   constexpr int kGemmBM = TL::kBM, kGemmBN = TL::kBN, kGemmWavesT = TL::kWavesT;
   constexpr int kWaveBF = TL::kBF, kWaveBT = TL::kBT;
@@ -369,10 +397,12 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void qkv_gemm_lds_ker
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(a.w), 0, static_cast<int>(3 * dim * dim * 2), kBufferRsrcFlags);
   const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<void*>(a.x), 0, static_cast<int>(a.n_x_rows * dim * 2), kBufferRsrcFlags);
+      const_cast<void*>(a.x), 0, static_cast<int>(BIG ? kMaxRangeBytes : a.n_x_rows * dim * 2), kBufferRsrcFlags);
   // Copy j of this wave: lane L fetches the logical chunk stored at physical chunk L % 8
-  // of tile row 8 * (wave * per + j) + L / 8; rows past the matrix read zeros.
+  // of tile row 8 * (wave * per + j) + L / 8; rows past the matrix read zeros (BIG:
+  // row 0, whose products are not stored).
   int w_off[kCopyW], a_off[kCopyA];
+  const uint16_t* a_ptr[BIG ? kCopyA : 1];
 #pragma unroll
   for (int j = 0; j < kCopyW; ++j) {
     const int row = 8 * (wave_s * kCopyW + j) + (lane >> 3);
@@ -386,14 +416,25 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void qkv_gemm_lds_ker
     const int lc = (lane & 7) ^ ((row >> 1) & 7);
     const long r = t_base + row;
     const long tok = r < a.n ? (a.rows ? static_cast<long>(a.rows[r]) : r) : 0;
-    a_off[j] = r < a.n ? static_cast<int>((tok * dim + lc * 8) * 2) : kOutOfRange;
+    if constexpr (BIG) {
+      a_ptr[j] = static_cast<const uint16_t*>(a.x) + tok * dim + lc * 8;
+      a_off[j] = 0;
+    } else {
+      a_off[j] = r < a.n ? static_cast<int>((tok * dim + lc * 8) * 2) : kOutOfRange;
+    }
   }
   auto copy_step = [&](uint16_t* wbuf, uint16_t* abuf, long k0) {
     const int so = static_cast<int>(k0 * 2);
 #pragma unroll
     for (int j = 0; j < kCopyW; ++j) lds_copy16(wrs, wbuf + (wave_s * kCopyW + j) * 8 * kGemmBK, w_off[j], so);
 #pragma unroll
-    for (int j = 0; j < kCopyA; ++j) lds_copy16(xrs, abuf + (wave_s * kCopyA + j) * 8 * kGemmBK, a_off[j], so);
+    for (int j = 0; j < kCopyA; ++j) {
+      uint16_t* dst = abuf + (wave_s * kCopyA + j) * 8 * kGemmBK;
+      if constexpr (BIG)
+        lds_copy16_global(a_ptr[j] + k0, dst);
+      else
+        lds_copy16(xrs, dst, a_off[j], so);
+    }
   };
 
   const int wc = wave / kGemmWavesT;  // feature slice of the block
@@ -451,10 +492,16 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void qkv_gemm_lds_ker
 template <typename TL>
 void launch_tile(const GemmArgs& a, const RowSource& src, long n, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>((a.ncols + TL::kBM - 1) / TL::kBM * ((n + TL::kBN - 1) / TL::kBN)));
-  if (src.eps) {
+  // bf16 token rows (and noise rows) beyond one buffer range
+  const bool big = src.n_x_rows * a.dim * 2 > kMaxRangeBytes;
+  if (src.eps && big) {
+    hipLaunchKernelGGL((qkv_gemm_kernel<kSrcRecover, TL, true>), grid, dim3(TL::kThreads), 0, s, a);
+  } else if (src.eps) {
     hipLaunchKernelGGL((qkv_gemm_kernel<kSrcRecover, TL>), grid, dim3(TL::kThreads), 0, s, a);
   } else if (src.x_dtype == kDtypeF32) {
     hipLaunchKernelGGL((qkv_gemm_kernel<kSrcF32, TL>), grid, dim3(TL::kThreads), 0, s, a);
+  } else if (big) {
+    hipLaunchKernelGGL((qkv_gemm_lds_kernel<TL, true>), grid, dim3(TL::kThreads), 0, s, a);
   } else {
     hipLaunchKernelGGL((qkv_gemm_lds_kernel<TL>), grid, dim3(TL::kThreads), 0, s, a);
   }

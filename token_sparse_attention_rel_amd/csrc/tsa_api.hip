@@ -192,8 +192,8 @@ tsa_status tsa_qkv_active(const void* x, int x_dtype, int64_t n_x_rows, const in
   if (dim <= 0 || dim % 64 != 0 || dim > (int64_t{1} << 20)) return TSA_ERR_SHAPE;
   if (!rows && n > n_x_rows) return TSA_ERR_SHAPE;
   if (out_is_cache && (n_cache < 0 || n_cache > kMaxRows)) return TSA_ERR_SHAPE;
-  // byte ranges of the token rows and of the weight must fit a 32-bit buffer range
-  if (n_x_rows * dim * 2 > kMaxBufferBytes || 3 * dim * dim * 2 > kMaxBufferBytes) return TSA_ERR_SHAPE;
+  // the weight is read through one 32-bit buffer range
+  if (3 * dim * dim * 2 > kMaxBufferBytes) return TSA_ERR_SHAPE;
   if (!aligned16(x) || !aligned16(w_qkv) || (q_out && !aligned16(q_out)) || !aligned16(k_out) ||
       !aligned16(v_out) || (eps && !aligned16(eps)) || (rows && !aligned4(rows)))
     return TSA_ERR_ALIGNMENT;
@@ -224,7 +224,7 @@ tsa_status tsa_qkv_active_rope(const void* x, int x_dtype, int64_t n_x_rows, con
   if (dim <= 0 || dim % 64 != 0 || dim > (int64_t{1} << 20)) return TSA_ERR_SHAPE;
   if (!rows && n > n_x_rows) return TSA_ERR_SHAPE;
   if (out_is_cache && (n_cache < 0 || n_cache > kMaxRows)) return TSA_ERR_SHAPE;
-  if (n_x_rows * dim * 2 > kMaxBufferBytes || 3 * dim * dim * 2 > kMaxBufferBytes) return TSA_ERR_SHAPE;
+  if (3 * dim * dim * 2 > kMaxBufferBytes) return TSA_ERR_SHAPE;
   if (!aligned16(x) || !aligned16(w_qkv) || (q_out && !aligned16(q_out)) || !aligned16(k_out) ||
       !aligned16(v_out) || (eps && !aligned16(eps)) || (rows && !aligned4(rows)))
     return TSA_ERR_ALIGNMENT;
@@ -247,7 +247,7 @@ tsa_status tsa_qkv_rows_to_cache(const tsa_bf16* a, int64_t n, int64_t dim, cons
   if (!a || !rows || !w_qkv || !k_cache || !v_cache) return TSA_ERR_INVALID_ARG;
   if (n < 0 || n > kMaxRows || n_cache < 0 || n_cache > kMaxRows) return TSA_ERR_SHAPE;
   if (dim <= 0 || dim % 64 != 0 || dim > (int64_t{1} << 20)) return TSA_ERR_SHAPE;
-  if (n * dim * 2 > kMaxBufferBytes || 3 * dim * dim * 2 > kMaxBufferBytes) return TSA_ERR_SHAPE;
+  if (3 * dim * dim * 2 > kMaxBufferBytes) return TSA_ERR_SHAPE;
   tsa::RopeSpec rope;
   if (heads != 0) {
     if (heads < 1 || heads > 4096 || dim % heads != 0 || (dim / heads) % 2 != 0 || dim / heads < 6)
@@ -296,7 +296,6 @@ tsa_status tsa_sparse_query_attention(const tsa_bf16* q, const tsa_bf16* k_cache
   if (heads < 1 || heads > 4096) return TSA_ERR_SHAPE;
   if (n_q < 0 || n_q > kMaxRows || n_kv < 1 || n_kv > kMaxRows) return TSA_ERR_SHAPE;
   if (out_rows && (n_out < 0 || n_out > kMaxRows)) return TSA_ERR_SHAPE;
-  if (n_kv * heads * static_cast<int64_t>(head_dim) * 2 > kMaxBufferBytes) return TSA_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
       (out_rows && !aligned4(out_rows)) || (lse_out && !aligned4(lse_out)) ||
       (workspace && !aligned16(workspace)))
@@ -322,7 +321,6 @@ tsa_status tsa_frame_causal_attention(const tsa_bf16* q, const tsa_bf16* k_cache
   if (n_q < 0 || n_q > kMaxRows || n_kv < 1 || n_kv > kMaxRows) return TSA_ERR_SHAPE;
   if (frame_tokens < 1 || frame_tokens > kMaxRows) return TSA_ERR_SHAPE;
   if (out_rows && (n_out < 0 || n_out > kMaxRows)) return TSA_ERR_SHAPE;
-  if (n_kv * heads * static_cast<int64_t>(head_dim) * 2 > kMaxBufferBytes) return TSA_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) || !aligned4(q_tokens) ||
       (out_rows && !aligned4(out_rows)) || (lse_out && !aligned4(lse_out)))
     return TSA_ERR_ALIGNMENT;
