@@ -77,8 +77,8 @@ def copy_calibration():
 
 
 ATTN_KERNELS = {
-    False: "attention_kernel<128> (active queries x all cached K/V, fused scatter)",
-    True: "attention_split_kernel<128> + attention_merge_kernel<128> (active queries x all cached "
+    False: "attention_kernel<128, false> (active queries x all cached K/V, fused scatter)",
+    True: "attention_split_kernel<128, false> + attention_merge_kernel<128> (active queries x all cached "
           "K/V, fused scatter; timed together)",
 }
 
