@@ -40,7 +40,7 @@ def _ulp(values, fmt):
 
 @pytest.mark.parametrize("state", ["f32", "bf16"])
 @pytest.mark.parametrize("n,dim,dt", [(1, 8, -0.125), (37, 200, 0.3), (1000, 1536, -0.0625),
-                                      (4099, 3072, -0.1234567), (3, 16, 0.0)])
+                                      (4099, 3072, -0.1234567), (3, 16, 0.0), (32760, 1536, -0.125)])
 def test_euler_matches_oracle(state, n, dim, dt):
     t = tsa()
     g = torch.Generator().manual_seed(n + dim)
@@ -209,6 +209,98 @@ def test_lipar_lif_pass_scaled():
         assert np.array_equal(o[f][~m[f]], o[f - 1][~m[f]])
 
 
+def _mask_flips_near_threshold(gm, want, cfg):
+    """Locations whose GPU mask (frames x hw) differs from the oracle's; the first frame that
+    differs at each must have a change score within 1e-5 (relative) of its threshold (later
+    frames follow from it through the long-term reference).  Returns their number."""
+    wm = want["mask"].reshape(cfg.frames, cfg.hw)
+    ws = want["short"].reshape(cfg.frames, cfg.hw)
+    wl = want["long"].reshape(cfg.frames, cfg.hw)
+    gm = gm.reshape(cfg.frames, cfg.hw)
+    flips = 0
+    for loc in np.flatnonzero((gm != wm).any(axis=0)):
+        f = int(np.argmax(gm[:, loc] != wm[:, loc]))
+        near = min(abs(ws[f, loc] - cfg.tau_short) / cfg.tau_short,
+                   abs(wl[f, loc] - cfg.tau_long) / cfg.tau_long)
+        assert near <= G.NEAR_THRESHOLD, (loc, f, ws[f, loc], wl[f, loc])
+        flips += 1
+    return flips
+
+
+@pytest.mark.slow
+def test_lipar_lif_pass_full_size():
+    """The long/short-term pass on the whole 33x45x80 clip (N = 118800, D = 3072, 24 heads):
+    mask, active and pruned lists bit for bit; the whole K/V cache (active rows projected from
+    their latent, pruned rows from their recovered rows) within the layer tolerance; 48 sampled
+    kept output rows and 48 sampled restored rows (each the output of the last kept frame at its
+    location) against the oracle, and each restored row bit-identical to its source row.
+    Where the masks differ (change scores within 1e-5 of a threshold) the pass after the mask
+    is rerun on the GPU with the oracle's mask."""
+    t = tsa()
+    cfg = configs.get_config("lipar_lif")
+    inp = generate.lipar_inputs(cfg, 0)
+    x, w = inp["x"], inp["w_qkv"]
+    eps = generate.lipar_eps(cfg, 0, 0)
+    print(f"  case {cfg.name} N={cfg.n} D={cfg.dim} heads={cfg.heads} frames={cfg.frames}", flush=True)
+    layer = t.PrunedAttentionLayer(cfg.n, cfg.dim, cfg.heads, G.dev(w))
+    xd, ed = G.dev(x), G.dev(eps)
+    got_k = layer.step_lipar_lif(xd, ed, cfg.frames, cfg.hw, cfg.tau_short, cfg.tau_long, cfg.sigma)
+    torch.cuda.synchronize()
+    x64, w64, e64 = G.host64(x), G.host64(w), G.host64(eps)
+    lm = ref.lif_mask(x64, cfg.frames, cfg.hw, cfg.tau_short, cfg.tau_long)
+    mask = lm["mask"]
+    k = int(mask.sum())
+    flips = _mask_flips_near_threshold(layer._lif_mask.cpu().numpy().astype(bool), lm, cfg)
+    print(f"  kept {k} of {cfg.n}; GPU kept {got_k}; near-threshold locations: {flips}", flush=True)
+    if flips:
+        md = G.dev(torch.from_numpy(mask.astype(np.uint8)))
+        for buf in (layer.k_cache, layer.v_cache, layer.out):
+            buf.zero_()
+        layer.select(None, mask=md)
+        layer._lipar_forward(xd, ed, cfg.hw, k, cfg.sigma, None)
+        t.restore_frames(layer.out, md, cfg.frames, cfg.hw)
+        torch.cuda.synchronize()
+    else:
+        assert got_k == k
+    idx, pidx = np.flatnonzero(mask), np.flatnonzero(~mask)
+    rng = np.random.default_rng(5)
+    kept_s = np.sort(rng.choice(idx, 48, replace=False))
+    pruned_s = np.sort(rng.choice(pidx[pidx >= cfg.hw], 48, replace=False))
+    m2 = mask.reshape(cfg.frames, cfg.hw)
+
+    def source(tok):  # the last kept frame at the token's location (frame 0 is always kept)
+        f, loc = divmod(int(tok), cfg.hw)
+        while not m2[f, loc]:
+            f -= 1
+        return f * cfg.hw + loc
+
+    src_s = np.array([source(p) for p in pruned_s])
+    need = np.unique(np.concatenate([kept_s, src_s]))
+    kc = np.zeros((cfg.n, cfg.dim))
+    vc = np.zeros((cfg.n, cfg.dim))
+    out = np.zeros((cfg.n, cfg.dim))
+    print(f"  oracle: projections of all {cfg.n} rows, attention of {need.size} queries", flush=True)
+    res = ref.lipar_step(x64, e64, w64, cfg.heads, cfg.hw, k, cfg.sigma, kc, vc, out,
+                         query_rows=np.searchsorted(idx, need), mask=mask)
+    out[need] = res["o_a"]
+    restored = ref.restore_frames(out, mask, cfg.frames, cfg.hw)
+    assert np.array_equal(layer.idx.cpu().numpy()[:k], res["idx"])
+    assert np.array_equal(layer.pidx.cpu().numpy()[:cfg.n - k], res["pidx"])
+    gk, gv = G.host64(layer.k_cache), G.host64(layer.v_cache)
+    G.assert_close(gk[idx], kc[idx], "K cache (active rows)", mabs=np.inf)
+    G.assert_close(gv[idx], vc[idx], "V cache (active rows)", mabs=np.inf)
+    for name, a, b in (("K", gk[pidx], kc[pidx]), ("V", gv[pidx], vc[pidx])):
+        rf = G.rel_frob(a, b)
+        rel_abs = float(np.max(np.abs(a - b) / np.maximum(1.0, np.abs(b))))
+        print(f"  {name} cache (recovered rows): rel_frob={rf:.3e} scaled max_abs={rel_abs:.3e}", flush=True)
+        assert rf <= G.REL_FROB and rel_abs <= G.MAX_ABS
+    del gk, gv
+    go = G.host64(layer.out)
+    G.assert_close(go[kept_s], restored[kept_s], "kept output rows")
+    G.assert_close(go[pruned_s], restored[pruned_s], "restored output rows")
+    assert np.array_equal(go[pruned_s], go[src_s])
+
+
 @pytest.mark.slow
 def test_lif_mask_full_size():
     """The 33x45x80 clip at D=3072: masks compared location by location up to the first
@@ -228,13 +320,7 @@ def test_lif_mask_full_size():
     ws = want["short"].reshape(cfg.frames, cfg.hw)
     wl = want["long"].reshape(cfg.frames, cfg.hw)
     gl = lo.cpu().numpy().astype(np.float64).reshape(cfg.frames, cfg.hw)
-    flips = 0
-    for loc in np.flatnonzero((gm != wm).any(axis=0)):
-        f = int(np.argmax(gm[:, loc] != wm[:, loc]))
-        near = min(abs(ws[f, loc] - cfg.tau_short) / cfg.tau_short,
-                   abs(wl[f, loc] - cfg.tau_long) / cfg.tau_long)
-        assert near <= G.NEAR_THRESHOLD, (loc, f, ws[f, loc], wl[f, loc])
-        flips += 1
+    flips = _mask_flips_near_threshold(gm, want, cfg)
     print(f"  kept {wm.sum()} of {wm.size}; near-threshold locations: {flips}", flush=True)
     same = ~(gm != wm).cumsum(axis=0).astype(bool)  # frames before the first disagreement
     fin = np.isfinite(wl) & same
