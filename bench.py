@@ -230,6 +230,10 @@ def hbm_kernels(tsa, torch, cfg, layer, xc, xp, sets=12, launches=20, reps=5):
                           4 * k * d * 2),
         "a8_scatter": (lambda i: tsa.scatter_out(kvs[i][0], idxs[i], k, caches[i][0]), 2 * k * d * 2),
     }
+    if xc.dtype != torch.bfloat16:
+        # fp32 token rows (the tiny workload) enter the projection directly; the standalone
+        # gather moves bf16 rows only
+        del ops["a4_gather"]
 
     def per_launch_ms(fn):
         for i in range(sets):
