@@ -76,11 +76,17 @@ def copy_calibration():
     return 0
 
 
-ATTN_KERNELS = {
-    False: "attention_kernel<128, false> (active queries x all cached K/V, fused scatter)",
-    True: "attention_split_kernel<128, false> + attention_merge_kernel<128> (active queries x all cached "
-          "K/V, fused scatter; timed together)",
-}
+def attention_kernel_label(cfg, split: bool, causal: bool) -> str:
+    """The attention kernel(s) the roofline object times, named as the profiler reports them."""
+    hd = cfg.head_dim
+    big = "true" if ((cfg.n - 1) * cfg.dim + hd) * 2 > 0x7FFFFFFF else "false"  # caches past one buffer range
+    if causal:
+        return (f"attention_causal_kernel<{hd}, {big}> (active queries x the keys of their frames and "
+                "earlier, fused scatter)")
+    if split:
+        return (f"attention_split_kernel<{hd}, {big}> + attention_merge_kernel<{hd}> (active queries x all "
+                "cached K/V, fused scatter; timed together)")
+    return f"attention_kernel<{hd}, {big}> (active queries x all cached K/V, fused scatter)"
 
 
 def _src_hash(path):
@@ -384,7 +390,7 @@ def bench_step(args, torch, tsa, cfg):
         "speedup_vs_dense": None if dense is None else round(dense["median"] / s_step["median"], 3),
         "roofline": {
             "bound": "mfma",
-            "kernel": ATTN_KERNELS[attn_ws is not None],
+            "kernel": attention_kernel_label(cfg, attn_ws is not None, cfg.causal),
             "achieved": round(achieved, 3),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
@@ -400,8 +406,6 @@ def bench_step(args, torch, tsa, cfg):
         },
     }
     if cfg.causal:
-        rec["roofline"]["kernel"] = ("attention_causal_kernel<128> (active queries x the keys of their "
-                                     "frames and earlier, fused scatter)")
         rec["attention_schedule"] = "one workgroup per query tile, key loop bounded by its queries' frames"
     if not args.no_cpu_baseline and not (cfg.rope or cfg.causal):
         rec["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_rows)
